@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 32] [--workload 1]
+
+A step is one pass of the whole path over one batch with every input resident in HBM:
+  indexer prolog (the batch's new query tokens and their key rows) -> Lightning Indexer
+  scores -> top-k -> sparse attention (+ split combine).
+The default workload is 4 sequences x 2 query tokens (MTP1) on 64K-token caches, indexer
+64 heads x 128 int8 with fp16 scales, top-k 2048, 128 attention heads over 576-wide bf16
+latent rows.  Inputs are seeded synthetic data of that shape.
+
+Cache honesty: the 256 MiB Infinity Cache (MALL) would hold one step's ~55 MB working set.
+The bench therefore keeps R copies of every input and output at distinct addresses and steps
+round-robin through them (R * per-step bytes >= 4x the MALL), so each step reads HBM.  The R
+steps are captured in one HIP graph that is replayed; the timed region is exactly `--steps`
+steps between two device synchronizations.
+
+Kernel timing: each kernel is also launched R times back to back (rotating copies) inside a
+graph bracketed by HIP events on the stream it runs on; the average per launch is reported
+per kernel, and the dominant one carries the roofline entry.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # dense int8 MFMA
+BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", type=int, default=1, help="named workload id (workloads.NAMED)")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input copies (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    from sparse_attention_14_amd import dsa
+    from sparse_attention_14_amd.step import IndexerCfg, StepBuffers, decode_step
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = workloads.named(args.workload)
+    sp = wl.spec
+    cfg = IndexerCfg(H=sp.H, D=sp.D, code=sp.code, scale_dt=sp.scale_dt,
+                     rope_dim=sp.rope_dim if sp.full_prolog else 0, rope_offset=sp.rope_offset,
+                     rope_interleaved=sp.rope_interleaved, hadamard=sp.full_prolog, k=sp.k)
+    d0 = workloads.device_arrays(wl, dev)
+    batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start, dev)
+    T, N, H, D, Hq, k = wl.T, wl.N, sp.H, sp.D, sp.Hq, sp.k
+    ct = torch.int8 if cfg.code == "i8" else torch.uint8
+    st = torch.float16 if cfg.scale_dt == "f16" else torch.float32
+    sbytes = 2 if cfg.scale_dt == "f16" else 4
+
+    # the quantized indexer key cache: every row through the prolog once (set-up, untimed)
+    k_cache = torch.empty((N, D), dtype=ct, device=dev)
+    k_scale = torch.empty((N,), dtype=st, device=dev)
+    dsa.dsa_indexer_prolog(H, D, cfg.code, cfg.scale_dt, k_in=d0["idx_k_in"], k_cos=d0["k_cos"],
+                           k_sin=d0["k_sin"], k_slot=d0["all_rows"], k_cache=k_cache,
+                           k_scale=k_scale, rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
+                           rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard)
+    new_q_in = d0["idx_q_in"]
+    new_k_in = d0["idx_k_in"][d0["new_rows"]].contiguous()
+    new_cos = d0["k_cos"][d0["new_rows"]].contiguous() if d0["k_cos"] is not None else None
+    new_sin = d0["k_sin"][d0["new_rows"]].contiguous() if d0["k_sin"] is not None else None
+
+    # per-step compulsory HBM bytes (strict roofline): K codes+scales scanned, new-token inputs,
+    # prolog outputs, scores written and read, gathered rows, attention q/out, indices
+    n_keys = int(np.sum(wl.q_pos[wl.q_start[1:] - 1] + 1))          # keys scanned per sequence
+    keff = np.minimum(k, wl.q_pos + 1)
+    n_sel = int(keff.sum())
+    score_cols = int(np.sum(wl.q_pos + 1))
+    in_b = 2 if wl.in_dtype == "bf16" else 4
+    b_prolog = T * H * D * in_b + T * D * in_b + T * H * (D + sbytes) + T * (D + sbytes)
+    b_indexer = n_keys * (D + sbytes) + T * H * (D + sbytes + 2) + score_cols * 4
+    b_topk = score_cols * 4 + T * k * 4
+    b_sfa = n_sel * 1152 + T * Hq * 576 * 2 + T * Hq * 512 * 2 + T * k * 4 + Hq * 4
+    step_bytes = b_prolog + b_indexer + b_topk + b_sfa
+    idx_ops = float(np.sum((wl.q_pos + 1).astype(np.float64))) * H * D * 2
+    sfa_flops = float(n_sel) * Hq * (576 + 512) * 2
+
+    R = args.sets or max(4, int(np.ceil(4 * MALL_BYTES / step_bytes)))
+    R = min(R, 32)
+
+    class Set:
+        pass
+
+    sets = []
+    for r in range(R):
+        s = Set()
+        s.k_cache = k_cache if r == 0 else k_cache.clone()
+        s.k_scale = k_scale if r == 0 else k_scale.clone()
+        s.kv = d0["kv"] if r == 0 else d0["kv"].clone()
+        s.q = d0["q"] if r == 0 else d0["q"].clone()
+        s.w = d0["w"] if r == 0 else d0["w"].clone()
+        s.q_in = new_q_in if r == 0 else new_q_in.clone()
+        s.k_in = new_k_in if r == 0 else new_k_in.clone()
+        s.buf = StepBuffers.alloc(batch, cfg, Hq, dev)
+        sets.append(s)
+    sink = d0["sink"]
+    new_slots = d0["new_rows"]
+
+    def step(s):
+        return decode_step(batch, cfg, q_in=s.q_in, k_in=s.k_in, new_slots=new_slots, w=s.w,
+                           k_cache=s.k_cache, k_scale=s.k_scale, q_attn=s.q, kv=s.kv, sink=sink,
+                           scale=wl.scale, buf=s.buf, q_cos=d0["q_cos"], q_sin=d0["q_sin"],
+                           k_cos=new_cos, k_sin=new_sin)
+
+    # stage launchers (for per-kernel timing)
+    def st_prolog(s):
+        dsa.dsa_indexer_prolog(H, D, cfg.code, cfg.scale_dt, q_in=s.q_in, q_cos=d0["q_cos"],
+                               q_sin=d0["q_sin"], q_codes=s.buf.q_codes, q_scale=s.buf.q_scale,
+                               k_in=s.k_in, k_cos=new_cos, k_sin=new_sin, k_slot=new_slots,
+                               k_cache=s.k_cache, k_scale=s.k_scale, rope_dim=cfg.rope_dim,
+                               rope_offset=cfg.rope_offset, rope_interleaved=cfg.rope_interleaved,
+                               hadamard=cfg.hadamard)
+
+    def st_indexer(s):
+        dsa.dsa_indexer_scores(batch, H, D, cfg.code, cfg.scale_dt, s.buf.q_codes, s.buf.q_scale,
+                               s.w, s.k_cache, s.k_scale, scores=s.buf.scores)
+
+    def st_topk(s):
+        dsa.dsa_topk(batch, s.buf.scores, k, idx=s.buf.idx, ws=s.buf.ws_topk)
+
+    def st_sfa(s):
+        dsa.dsa_sparse_attn_decode(batch, s.q, s.kv, s.buf.idx, sink, wl.scale, out=s.buf.out,
+                                   ws=s.buf.ws_sfa)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ref = step(sets[0]).clone()
+        for s in sets[1:]:
+            step(s)
+    torch.cuda.synchronize()
+    for s in sets:
+        assert torch.equal(s.buf.out, ref), "rotating copies disagree"
+
+    def capture(fn_per_set):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s in sets:
+                fn_per_set(s)
+        return g
+
+    def replay(g, n):
+        # CUDAGraph.replay() launches on torch's current stream: make it the timed stream
+        with torch.cuda.stream(stream):
+            for _ in range(n):
+                g.replay()
+
+    g_step = capture(step)
+    # replay check: several replays with eager work and syncs between, all equal to eager
+    for rep in range(3):
+        for s in sets:
+            s.buf.out.zero_()
+        torch.cuda.synchronize()
+        replay(g_step, 1)
+        torch.cuda.synchronize()
+        for s in sets:
+            assert torch.equal(s.buf.out, ref), f"graph replay {rep} differs from eager"
+
+    # warm-up and timed region: K steps = K / R replays of the R-step graph
+    reps_w = max(1, args.warmup // R)
+    reps = max(1, int(round(args.steps / R)))
+    K = reps * R
+    replay(g_step, reps_w)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    replay(g_step, reps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_step = e0.elapsed_time(e1) * 1000.0 / K
+
+    # per-stage / per-kernel timing: R launches of one stage per graph replay
+    stages = {"prolog": st_prolog, "indexer": st_indexer, "topk": st_topk, "sfa": st_sfa}
+    stage_us = {}
+    for name, fn in stages.items():
+        g = capture(fn)
+        replay(g, 3)
+        torch.cuda.synchronize()
+        n = max(4, 64 // R)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        replay(g, n)
+        b.record(stream)
+        torch.cuda.synchronize()
+        stage_us[name] = a.elapsed_time(b) * 1000.0 / (n * R)
+    # the graphs of the stages replaced the step's results; restore and re-check once
+    replay(g_step, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(sets[0].buf.out, ref)
+
+    idx_tops = idx_ops / (stage_us["indexer"] * 1e-6) / 1e12
+    sfa_gbps = n_sel * 1152 / (stage_us["sfa"] * 1e-6) / 1e9
+    dominant = max(("indexer", "sfa"), key=lambda n: stage_us[n])
+    dom_bytes = b_indexer if dominant == "indexer" else b_sfa
+    dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
+    kernel_name = {"indexer": "dsa::indexer_kernel", "sfa": "dsa::sfa_kernel"}[dominant]
+
+    result = {
+        "metric": "DSA decode us/step at B=4,64K ctx; indexer int8 TOPS; SFA gathered-KV GB/s",
+        "value": round(us_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": reps_w * R,
+        "ms_per_step": round(us_step / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if cfg.code == "i8" else "fp8(e4m3)->bf16",
+        "data": "synthetic",
+        "config": {"workload": sp.name, "B": wl.B, "query_tokens": T, "kv_len_max": wl.max_kv_len,
+                   "indexer": f"{H}x{D} {cfg.code} codes, {cfg.scale_dt} scales",
+                   "topk": k, "attn_heads": Hq, "d_qk": 576, "d_v": 512,
+                   "prolog": "rope+hadamard+quant" if sp.full_prolog else "quant",
+                   "rotating_input_sets": R, "per_step_hbm_bytes": step_bytes},
+        "step_roofline_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "stage_us": {n: round(v, 3) for n, v in stage_us.items()},
+        "indexer_tops": round(idx_tops, 2),
+        "indexer_tops_frac": round(idx_tops / (INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS), 4),
+        "sfa_gathered_GBps": round(sfa_gbps, 1),
+        "sfa_gathered_frac": round(sfa_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(stage_us[dominant], 3)},
+        "wall_s_timed": round(wall, 4),
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The oracle's decode step on the host cores (prolog of the new tokens and rows, indexer
+    over every visible key, top-k, attention), repeated while within the time budget."""
+    import oracle
+    from oracle.step import prolog_inputs_f64
+    from threadpoolctl import threadpool_info
+    sp = wl.spec
+    oq = oracle.step.quantize_workload(wl)          # cache state from earlier steps (untimed)
+    q_in, k_in = prolog_inputs_f64(wl)
+    rows = wl.new_rows()
+    rope = sp.rope_dim if sp.full_prolog else 0
+    n, t_tot = 0, 0.0
+    while t_tot < budget_s and n < 50:
+        t0 = time.perf_counter()
+        nq = oracle.indexer_prolog(q_in, k_in[rows], wl.q_cos, wl.q_sin,
+                                   None if wl.k_cos is None else wl.k_cos[rows],
+                                   None if wl.k_sin is None else wl.k_sin[rows], rope,
+                                   sp.rope_offset, sp.rope_interleaved, sp.full_prolog, sp.code,
+                                   sp.scale_dt)
+        oq["k_codes"][rows] = nq["k_codes"]
+        oq["k_scale"][rows] = nq["k_scale"]
+        sc = oracle.indexer_scores(nq["q_codes"], nq["q_scale"], wl.w, oq["k_codes"], oq["k_scale"],
+                                   sp.code, wl.q_seq, wl.q_pos, wl.kv_start)
+        idx = oracle.topk_select(sc, sp.k)
+        oracle.sparse_attention(wl.q, wl.kv, idx, wl.q_seq, wl.kv_start, wl.sink, wl.scale)
+        t_tot += time.perf_counter() - t0
+        n += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(t_tot / n * 1e6, 1), "unit": "us/step", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full decode steps of the same workload ({wl.T} query tokens), "
+                      f"float64 numpy oracle, cache quantization excluded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek sparse-attention (DSA) decode path.
+ *
+ * The path (one decode step of a DSA layer):
+ *   dsa_indexer_prolog      RoPE -> Hadamard -> per-token-head dynamic int8/fp8 quant of the
+ *                           indexer query and of the new key rows (written into the key cache)
+ *   dsa_indexer_scores      Lightning Indexer: int8/fp8 dot products of every query head against
+ *                           every visible cached key, ReLU, head-weighted sum
+ *   dsa_topk                per query token, the k highest-scoring visible positions
+ *   dsa_sparse_attn_decode  attention of 128 (or 16) query heads over the selected 576-wide MLA
+ *                           latent rows, online softmax in fp32, per-head attention sink
+ *
+ * Sources, cited by page title and section:
+ *   [SFA] "NPU DeepSeek-V4 TileLang算子开发实践" (mooersco.com/news/996258), 1 Sparse Flash
+ *         Attention: I/O tensors and algorithm steps 1-8.
+ *   [AQ]  same page, 4 Activation Quantization, steps 1-3.
+ *   [PRO] "NPU DeepSeek-V3.2-Exp PyPTO 融合算子开发优化实践" (jsqmd.com/news/787325), Indexer
+ *         Prolog: formulas and quantization strategy.
+ *   [LI]  same page, Lightning Indexer.   [DIA] same page, Deepseek Indexer Attention.
+ *   [ARCH] ops-tilelang docs/architecture.md: public-API duties (validate every argument,
+ *         compute launch parameters on the host, empty inputs are defined no-ops).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are device (HBM) pointers; everything else is host memory.
+ *  - The caller owns and allocates every buffer and keeps it alive until the stream has
+ *    passed the work.  The library never allocates, frees or synchronizes, keeps no pointer
+ *    after returning, and only enqueues kernels on `stream` (a hipStream_t; NULL = default).
+ *  - Arrays are dense row-major.  Row pointers and row strides must be 16-byte aligned.
+ *  - Validation failures return before any HIP call, write nothing, and leave a message in
+ *    dsa_last_error().  A HIP launch error returns DSA_ERR_HIP with hipGetErrorString text.
+ *    Values inside device arrays (indices, positions) are not checked: out-of-range values
+ *    there are undefined behaviour, as for any kernel input.
+ *  - A call with zero query tokens (or zero rows) is a successful no-op.
+ *  - Calls on the same stream are ordered; calls that share a workspace buffer must not run
+ *    concurrently on different streams.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, inconsistent sizes   */
+  DSA_ERR_UNSUPPORTED = 2,   /* a valid request outside the compiled set (head counts...)  */
+  DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_size()       */
+  DSA_ERR_HIP = 4            /* a HIP runtime error while enqueuing                        */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_I8 = 1,                /* int8 code                                                  */
+  DSA_FP8_E4M3 = 2,          /* OCP fp8 E4M3FN code (max 448)                              */
+  DSA_F16 = 3,
+  DSA_BF16 = 4,
+  DSA_F32 = 5
+} dsa_dtype;
+
+/*
+ * A ragged decode batch over flat per-sequence caches.
+ * Sequence b owns cache rows kv_start[b] .. kv_start[b] + L_b - 1 of the key cache and of the
+ * latent KV cache; its query tokens are t = q_start[b] .. q_start[b+1]-1 (contiguous), and
+ * token t sees its sequence's positions 0 .. q_pos[t] (causal; its own row included, since
+ * the prolog writes a token's key row before the indexer runs -- [DIA] order).
+ */
+typedef struct dsa_batch {
+  int32_t num_seqs;          /* B >= 0 (host)                                              */
+  int32_t num_q;             /* T >= 0 (host), = q_start[B]                                */
+  int32_t max_q_per_seq;     /* host: max_b (q_start[b+1] - q_start[b]), >= 1 if T > 0    */
+  int32_t max_kv_len;        /* host: max_t q_pos[t] + 1 (score columns used, grid sizing) */
+  const int32_t* q_start;    /* device [B+1], q_start[0] = 0, non-decreasing               */
+  const int32_t* q_seq;      /* device [T]: the sequence of token t                        */
+  const int32_t* q_pos;      /* device [T]: position p_t of token t, 0 <= p_t < max_kv_len */
+  const int64_t* kv_start;   /* device [B]: first cache row of sequence b                  */
+} dsa_batch;
+
+/* ---------------------------------------------------------------- indexer prolog ---------- */
+/*
+ * [PRO] Indexer Prolog, from RoPE on:  codes, scale = DynamicQuant(Hadamard(RoPE(x)))
+ * per (token, head) for the indexer query and per token for the indexer key ("C8" cache).
+ * [AQ] steps 1-3 define the quantizer: fp32, amax over the row, scale = amax / 127 (int8) or
+ * amax / 448 (e4m3), optional power-of-two rounding of the scale, codes = round-half-even(
+ * clamp(x / scale, -max, max)); an all-zero row gets scale 0 and zero codes.
+ * RoPE and the Hadamard are evaluated in fp64 and rounded once to fp32 before the quantizer.
+ * The stored scale is the fp32 scale rounded to scale_dtype (fp16 per [PRO], or fp32).
+ */
+typedef struct dsa_prolog_cfg {
+  int32_t H;                 /* query heads (key rows have one head)                      */
+  int32_t D;                 /* head dim: 64 or 128                                       */
+  int32_t rope_dim;          /* 0 = no RoPE, else even, rope_offset + rope_dim <= D       */
+  int32_t rope_offset;       /* first rotated dim (64 = the last 64 dims of 128)          */
+  int32_t rope_interleaved;  /* 0: pairs (i, i + rope_dim/2);  1: pairs (2i, 2i + 1)      */
+  int32_t hadamard;          /* 1: right-multiply by the orthonormal Sylvester Hadamard_D */
+  int32_t round_scale;       /* 1: scale rounded up to a power of two                    */
+  dsa_dtype in_dtype;        /* DSA_BF16 or DSA_F32 activations                           */
+  dsa_dtype code_dtype;      /* DSA_I8 or DSA_FP8_E4M3                                    */
+  dsa_dtype scale_dtype;     /* DSA_F16 or DSA_F32                                        */
+} dsa_prolog_cfg;
+
+/*
+ * Query part (num_q > 0): q_in device [num_q, H, D] in_dtype -> q_codes device [num_q, H, D]
+ *   (1 byte each), q_scale device [num_q, H] scale_dtype.  q_cos/q_sin device
+ *   [num_q, rope_dim/2] fp32 (ignored when rope_dim == 0).
+ * Key part (num_k > 0): k_in device [num_k, D] in_dtype; row r is written to cache row
+ *   k_slot[r] (device int64) of k_cache device [*, D] and k_scale device [*].  k_cos/k_sin
+ *   device [num_k, rope_dim/2] fp32.
+ * Either part may be empty (its pointers are then ignored).
+ */
+dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg,
+                              int32_t num_q, const void* q_in, const float* q_cos,
+                              const float* q_sin, void* q_codes, void* q_scale,
+                              int32_t num_k, const void* k_in, const float* k_cos,
+                              const float* k_sin, const int64_t* k_slot, void* k_cache,
+                              void* k_scale, void* stream);
+
+/* ---------------------------------------------------------------- lightning indexer ------- */
+/*
+ * [LI] (scores before TopK), operands from [PRO]:
+ *   D[t,h,s] = sum_d q[t,h,d] k[s,d]                       (int32-exact for int8 codes)
+ *   I[t,s]   = sum_h w[t,h] * ReLU(q_scale[t,h] * k_scale[s] * D[t,h,s]),   s = 0 .. p_t
+ * evaluated as k_scale[s] * sum_h (w*q_scale)[t,h] * max(D[t,h,s], 0) in fp32 (the scales are
+ * positive).  Supported: (H, D) in {(64,128), (8,64)}; codes DSA_I8 (int8 MFMA) or
+ * DSA_FP8_E4M3 (fp8 MFMA); scales DSA_F16 or DSA_F32; w is fp16.
+ *   q_codes  device [T, H, D]          q_scale device [T, H]        w device [T, H] fp16
+ *   k_cache  device [N, D] (rows of every sequence, see dsa_batch)  k_scale device [N]
+ *   scores   device [T, ld] fp32, ld >= max_kv_len, ld % 4 == 0.  Row t gets columns 0 .. p_t;
+ *            columns past p_t are not written.
+ */
+dsa_status dsa_indexer_scores(const dsa_batch* batch, int32_t H, int32_t D,
+                              dsa_dtype code_dtype, dsa_dtype scale_dtype,
+                              const void* q_codes, const void* q_scale, const void* w,
+                              const void* k_cache, const void* k_scale,
+                              float* scores, int64_t ld, void* stream);
+
+/*
+ * Test hook for the bit-exactness rule: the same int8 MFMA contraction as
+ * dsa_indexer_scores, writing the raw int32 dot products dots[t, h, s] (device
+ * [T, H, ld] int32, s = 0 .. p_t) instead of the weighted scores.  int8 codes only.
+ */
+dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
+                                const int8_t* q_codes, const int8_t* k_cache,
+                                int32_t* dots, int64_t ld, void* stream);
+
+/* ---------------------------------------------------------------- top-k ------------------- */
+/*
+ * [LI] TopK; [SFA] step 2 index convention.  For every token t: the k_eff = min(k, p_t + 1)
+ * positions s in 0 .. p_t with the largest scores[t, s]; equal scores go to the lower
+ * position; the set is written to idx[t, 0 .. k_eff) in ascending position order and
+ * idx[t, k_eff .. k) = -1.  Selection is exact on the fp32 scores (radix select over
+ * order-preserving keys; -0.0 equals +0.0).  1 <= k <= 2048.
+ *   scores device [T, ld] fp32 (as written by dsa_indexer_scores), idx device [T, k] int32.
+ *   ws: device workspace of at least dsa_topk_workspace_size(T, max_kv_len, k) bytes,
+ *       256-byte aligned; contents need no initialisation and are scratch afterwards.
+ */
+size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k);
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- sparse attention -------- */
+/*
+ * [SFA] steps 1-8 with the attention sink of step 7 read as a per-head logit that joins the
+ * softmax denominator:  for J_t = { idx[t, j] != -1 },
+ *   z_j = scale * q[t,h,:576] . kv[row_j, :576],   row_j = kv_start[seq(t)] + idx[t, j]
+ *   o[t,h,:] = sum_j e^{z_j} kv[row_j, :512] / (sum_j e^{z_j} + e^{sink[h]})
+ * (MLA absorbed form: one latent KV head of 576 = 512 nope + 64 rope columns shared by all
+ * query heads; the value is the first 512 columns).  Empty J_t gives 0.  QK^T and PV run on
+ * bf16 MFMA with fp32 accumulation; the softmax is online in fp32; probabilities enter PV
+ * as bf16.
+ *   q      device [T, Hq, 576] bf16         Hq in {16, 128}
+ *   kv     device rows of 576 bf16, row r at kv + r * kv_row_stride elements
+ *          (kv_row_stride >= 576, multiple of 8)
+ *   idx    device [T, k] int32 (positions within the token's sequence, -1 = skip), 1 <= k <= 2048
+ *   sink   device [Hq] fp32, or NULL for no sink
+ *   out    device [T, Hq, 512] bf16
+ *   ws:    device workspace of at least dsa_sparse_attn_workspace_size(T, Hq, k) bytes,
+ *          256-byte aligned (split-K partials); may be NULL when that size is 0.
+ */
+size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int32_t k);
+dsa_status dsa_sparse_attn_decode(const dsa_batch* batch, int32_t Hq, const void* q,
+                                  const void* kv, int64_t kv_row_stride, const int32_t* idx,
+                                  int32_t k, const float* sink, float scale, void* out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc -------------------- */
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+/* Library version string. */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,84 @@
+"""ctypes loader for libdsa.so and the C structs of include/dsa.h.
+
+The library must exist (build it with `python -m sparse_attention_14_amd.build`); there is
+no fallback of any kind -- importing this module without it raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+# dsa_status
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, 1, 2, 3, 4
+STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
+                3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
+# dsa_dtype
+DSA_I8, DSA_FP8_E4M3, DSA_F16, DSA_BF16, DSA_F32 = 1, 2, 3, 4, 5
+
+
+class DsaBatch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q", ctypes.c_int32),
+                ("max_q_per_seq", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+                ("q_start", ctypes.c_void_p), ("q_seq", ctypes.c_void_p),
+                ("q_pos", ctypes.c_void_p), ("kv_start", ctypes.c_void_p)]
+
+
+class DsaPrologCfg(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("D", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("rope_offset", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32),
+                ("hadamard", ctypes.c_int32), ("round_scale", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int), ("code_dtype", ctypes.c_int),
+                ("scale_dtype", ctypes.c_int)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_BP = ctypes.POINTER(DsaBatch)
+
+# name -> (restype, argtypes); mirrors include/dsa.h
+SIGNATURES = {
+    "dsa_indexer_prolog": (ctypes.c_int, [ctypes.POINTER(DsaPrologCfg), _I32, _P, _P, _P, _P, _P,
+                                          _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "dsa_indexer_scores": (ctypes.c_int, [_BP, _I32, _I32, ctypes.c_int, ctypes.c_int, _P, _P, _P,
+                                          _P, _P, _P, _I64, _P]),
+    "dsa_indexer_dots_i32": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "dsa_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "dsa_topk": (ctypes.c_int, [_BP, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "dsa_sparse_attn_decode": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
+                                              ctypes.c_float, _P, _P, _SZ, _P]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_version": (ctypes.c_char_p, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                          f"(python -m sparse_attention_14_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib.dsa_last_error().decode(errors="replace")
+        super().__init__(f"{fn} -> {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def check(fn: str, status: int) -> None:
+    if status != DSA_OK:
+        raise DsaError(fn, status)

@@ -1,0 +1,58 @@
+// Shared device/host helpers of the gfx950 DSA kernels (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short u16;
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32.  bf16 is the upper half of an fp32; widening is exact.
+__device__ __forceinline__ float bf16_to_f32(u16 b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<u16>(u >> 16);
+}
+
+// fp16 <-> fp32 (IEEE binary16; narrowing rounds to nearest even).
+__device__ __forceinline__ float f16_bits_to_f32(u16 h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ u16 f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(u16, static_cast<_Float16>(f));
+}
+
+// Flat workgroup id remapped so that consecutive logical ids land on one XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8); logical id
+// w = xcd * per_xcd + slot keeps neighbours (which share data) in one L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int per = (n + 7) / 8;
+  const int xcd = id % 8, slot = id / 8;
+  const int full = n % 8 == 0 ? 8 : n % 8;           // XCDs that hold `per` items
+  int w = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+  return w;
+}
+
+}  // namespace dsa
+
+// Host-side helpers (defined in api.hip).
+namespace dsa_host {
+dsa_status fail(dsa_status st, const char* fmt, ...);
+dsa_status check_launch(const char* what);
+}  // namespace dsa_host

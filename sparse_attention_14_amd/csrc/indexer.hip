@@ -1,0 +1,278 @@
+// Lightning Indexer scores on gfx950 (int8 MFMA; fp8 codes through exact bf16 MFMA).
+//
+// [LI] "Lightning Indexer" (jsqmd.com/news/787325): per query token, the quantized query of
+// every indexer head is multiplied against the quantized key cache, followed by ReLU, a
+// per-head weighting and a sum over heads; [PRO] gives the operands (per-token-head codes
+// with fp16 dequant factors, fp16 head weights).
+//
+//   I[t,s] = k_scale[s] * sum_h (w * q_scale)[t,h] * max(D[t,h,s], 0),  D = q[t,h,:] . k[s,:]
+//
+// Work decomposition (decode and prefill shapes alike): a workgroup owns one sequence, a group
+// of G of its query tokens and a chunk of CK = 512 cached keys.  Its 4 waves split the chunk's
+// 32-key blocks; a wave keeps one token's query codes (all heads) resident in VGPRs as the MFMA
+// A operand and streams key rows straight from HBM into VGPRs as the B operand -- every key
+// byte is read from HBM once per token group, with no LDS round trip.  The head reduction is
+// fused: the 32x32 accumulator puts 16 heads of one key in a lane and the other 16 in lane
+// l^32, so the weighted ReLU sum is 16 FMAs per M-block plus a single cross-lane add.
+//
+// MFMA k-permutation: the contraction runs over all D dims, so A and B only need the same
+// (lane, byte) -> d assignment.  Lane half hv = lane/32 owns dims [hv*D/2, hv*D/2 + D/2) of
+// both the query row and the key row, so each lane reads D/2 contiguous bytes of its key row.
+#include "common.h"
+
+namespace dsa {
+
+struct IdxArgs {
+  const int32_t* q_start; const int32_t* q_pos; const int64_t* kv_start;
+  const uint8_t* q_codes; const void* q_scale; const u16* w;
+  const uint8_t* k_cache; const void* k_scale;
+  float* scores; int32_t* dots; long ld;
+  int H; int ngrp; int scale_f16;
+};
+
+constexpr int kCK = 512;     // keys per workgroup
+constexpr int kBlk = 32;     // keys per MFMA column block
+
+// Per-lane operand of one 32x32 block: this lane's D/2 code bytes.
+//  int8: D/32 MFMAs v_mfma_i32_32x32x32_i8 (k = 32, 16 bytes per lane each), exact int32.
+//  fp8 : the bytes are widened to bf16 in registers (every e4m3 value is exactly a bf16;
+//        v_cvt_scalef32_pk_bf16_fp8 with unit scale converts two codes per instruction) and
+//        contracted on v_mfma_f32_32x32x16_bf16 (k = 16): products are exact in fp32 and the
+//        sums carry fp32 rounding only.  The fp8 MFMA itself accumulates with a narrower
+//        internal adder (about 2e-5 relative error on these dots), too coarse for the top-k
+//        near-tie tolerance, so it is not used here.
+template <bool FP8, int D>
+struct KFrag;
+template <int D>
+struct KFrag<false, D> { v4i v[D / 32]; };
+template <int D>
+struct KFrag<true, D> { v8bf v[D / 16]; };
+
+template <int D>
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <bool FP8, int D>
+__device__ __forceinline__ void load_row_half(KFrag<FP8, D>& f, const uint8_t* p) {
+  // p: 16-byte aligned start of this lane's D/2 bytes
+  const v4i* q = reinterpret_cast<const v4i*>(p);
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) f.v[j] = q[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const v4i w = q[j];
+      f.v[2 * j] = fp8x8_to_bf16<D>(w[0], w[1]);
+      f.v[2 * j + 1] = fp8x8_to_bf16<D>(w[2], w[3]);
+    }
+  }
+}
+
+template <bool FP8>
+struct AccT;
+template <> struct AccT<false> { typedef v16i type; };
+template <> struct AccT<true> { typedef v16f type; };
+
+template <bool FP8, int D>
+__device__ __forceinline__ typename AccT<FP8>::type mma_block(const KFrag<FP8, D>& a,
+                                                             const KFrag<FP8, D>& b) {
+  typename AccT<FP8>::type c = {};
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a.v[j], b.v[j], c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v[j], b.v[j], c, 0, 0, 0);
+  }
+  return c;
+}
+
+// G = query tokens per workgroup (1, 2, 4); NMB = 32-head M-blocks per token (ceil(H/32)).
+template <int G, int NMB, int D, bool FP8, bool DOTS>
+__global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
+  constexpr int NPH = 4 / G;                 // waves sharing one token
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hv = lane >> 5, col = lane & 31;
+  const int b = blockIdx.y / a.ngrp, g = blockIdx.y % a.ngrp;
+  const int q_lo = a.q_start[b] + g * G, q_hi = a.q_start[b + 1];
+  if (q_lo >= q_hi) return;
+  int maxp = -1;
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
+  const int chunk0 = blockIdx.x * kCK;
+  if (chunk0 > maxp) return;
+  const int t = q_lo + wave % G;
+  if (t >= q_hi) return;
+  const int phase = wave / G;
+  const int p = a.q_pos[t];
+  const long kv0 = a.kv_start[b];
+  const int H = a.H;
+
+  // query codes of token t: M-block mb, row col -> head 32 mb + col
+  KFrag<FP8, D> qf[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int h = 32 * mb + col;
+    if (h < H) {
+      load_row_half<FP8, D>(qf[mb], a.q_codes + ((long)t * H + h) * D + hv * (D / 2));
+    } else {
+#pragma unroll
+      for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[mb].v[j] = {};
+    }
+  }
+  // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane
+  float wq[NMB][16];
+  if constexpr (!DOTS) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
+        float v = 0.f;
+        if (h < H) {
+          const long o = (long)t * H + h;
+          const float qs = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.q_scale)[o])
+                                       : ((const float*)a.q_scale)[o];
+          v = f16_bits_to_f32(a.w[o]) * qs;
+        }
+        wq[mb][i] = v;
+      }
+  }
+
+  for (int kb = phase; kb < kCK / kBlk; kb += NPH) {
+    const int s0 = chunk0 + kb * kBlk;
+    if (s0 > p) break;
+    const int s = s0 + col;
+    const long row = kv0 + min(s, p);                     // clamp: stay inside the sequence
+    KFrag<FP8, D> kf;
+    load_row_half<FP8, D>(kf, a.k_cache + row * D + hv * (D / 2));
+    float ks = 0.f;
+    if constexpr (!DOTS)
+      ks = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+    if constexpr (DOTS) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const auto acc = mma_block<FP8, D>(qf[mb], kf);
+        if (s <= p) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
+            if (h < H) a.dots[((long)t * H + h) * a.ld + s] = (int32_t)acc[i];
+          }
+        }
+      }
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const auto acc = mma_block<FP8, D>(qf[mb], kf);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float d;
+          if constexpr (FP8) d = fmaxf(acc[i], 0.f);
+          else d = (float)max(acc[i], 0);
+          sum = fmaf(wq[mb][i], d, sum);
+        }
+      }
+      sum += __shfl_xor(sum, 32, kWave);
+      if (hv == 0 && s <= p) a.scores[(long)t * a.ld + s] = sum * ks;
+    }
+  }
+}
+
+template <int G, int NMB, int D, bool FP8, bool DOTS>
+static void launch(const IdxArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS>), grid, dim3(256), 0, st, a);
+}
+
+template <int NMB, int D, bool FP8, bool DOTS>
+static void launch_g(int G, const IdxArgs& a, dim3 grid, hipStream_t st) {
+  if (G == 1) launch<1, NMB, D, FP8, DOTS>(a, grid, st);
+  else if (G == 2) launch<2, NMB, D, FP8, DOTS>(a, grid, st);
+  else launch<4, NMB, D, FP8, DOTS>(a, grid, st);
+}
+
+}  // namespace dsa
+
+using dsa_host::fail;
+
+static dsa_status check_batch(const dsa_batch* bt, const char* fn) {
+  if (!bt) return fail(DSA_ERR_INVALID_ARG, "%s: batch is NULL", fn);
+  if (bt->num_seqs < 0 || bt->num_q < 0) return fail(DSA_ERR_INVALID_ARG, "%s: negative batch size", fn);
+  if (bt->num_q > 0) {
+    if (bt->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "%s: tokens without sequences", fn);
+    if (!bt->q_start || !bt->q_seq || !bt->q_pos || !bt->kv_start)
+      return fail(DSA_ERR_INVALID_ARG, "%s: a batch array is NULL", fn);
+    if (bt->max_q_per_seq < 1 || bt->max_q_per_seq > bt->num_q)
+      return fail(DSA_ERR_INVALID_ARG, "%s: max_q_per_seq out of range (%d)", fn, bt->max_q_per_seq);
+    if (bt->max_kv_len < 1) return fail(DSA_ERR_INVALID_ARG, "%s: max_kv_len must be >= 1", fn);
+  }
+  return DSA_OK;
+}
+
+// exported for the other translation units
+dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn) { return check_batch(bt, fn); }
+
+static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype code, dsa_dtype sdt,
+                                 const void* q, const void* qs, const void* w, const void* k,
+                                 const void* ks, float* scores, int32_t* dots, bool want_dots,
+                                 long ld, void* stream, const char* fn) {
+  dsa_status st = check_batch(bt, fn);
+  if (st != DSA_OK) return st;
+  if (!((H == 64 && D == 128) || (H == 8 && D == 64)))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: (H, D) = (%d, %d) not compiled; supported (64,128), (8,64)", fn, H, D);
+  if (code != DSA_I8 && code != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "%s: code dtype must be I8 or FP8_E4M3", fn);
+  if (!want_dots && sdt != DSA_F16 && sdt != DSA_F32) return fail(DSA_ERR_UNSUPPORTED, "%s: scale dtype must be F16 or F32", fn);
+  if (bt->num_q == 0) return DSA_OK;
+  if (!q || !k || (want_dots ? !dots : (!qs || !w || !ks || !scores)))
+    return fail(DSA_ERR_INVALID_ARG, "%s: a data pointer is NULL", fn);
+  if (ld < bt->max_kv_len) return fail(DSA_ERR_INVALID_ARG, "%s: ld (%ld) < max_kv_len (%d)", fn, ld, bt->max_kv_len);
+  if (!want_dots && (ld % 4)) return fail(DSA_ERR_INVALID_ARG, "%s: ld must be a multiple of 4", fn);
+  if (((uintptr_t)q | (uintptr_t)k) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q/k codes must be 16-byte aligned", fn);
+
+  dsa::IdxArgs a{};
+  a.q_start = bt->q_start; a.q_pos = bt->q_pos; a.kv_start = bt->kv_start;
+  a.q_codes = (const uint8_t*)q; a.q_scale = qs; a.w = (const dsa::u16*)w;
+  a.k_cache = (const uint8_t*)k; a.k_scale = ks; a.scores = scores; a.dots = dots; a.ld = ld;
+  a.H = H; a.scale_f16 = sdt == DSA_F16;
+  const int G = bt->max_q_per_seq >= 3 ? 4 : bt->max_q_per_seq;
+  a.ngrp = (bt->max_q_per_seq + G - 1) / G;
+  const long gy = (long)bt->num_seqs * a.ngrp;
+  if (gy > 65535L) return fail(DSA_ERR_INVALID_ARG, "%s: too many token groups", fn);
+  const dim3 grid((unsigned)((bt->max_kv_len + dsa::kCK - 1) / dsa::kCK), (unsigned)gy);
+  hipStream_t s = (hipStream_t)stream;
+  const bool fp8 = code == DSA_FP8_E4M3;
+  if (D == 128) {
+    if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_g<2, 128, false, true>(G, a, grid, s); }
+    else if (fp8) dsa::launch_g<2, 128, true, false>(G, a, grid, s);
+    else dsa::launch_g<2, 128, false, false>(G, a, grid, s);
+  } else {
+    if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_g<1, 64, false, true>(G, a, grid, s); }
+    else if (fp8) dsa::launch_g<1, 64, true, false>(G, a, grid, s);
+    else dsa::launch_g<1, 64, false, false>(G, a, grid, s);
+  }
+  return dsa_host::check_launch(fn);
+}
+
+extern "C" dsa_status dsa_indexer_scores(const dsa_batch* batch, int32_t H, int32_t D,
+                                         dsa_dtype code_dtype, dsa_dtype scale_dtype,
+                                         const void* q_codes, const void* q_scale, const void* w,
+                                         const void* k_cache, const void* k_scale, float* scores,
+                                         int64_t ld, void* stream) {
+  return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                        k_scale, scores, nullptr, false, ld, stream, "dsa_indexer_scores");
+}
+
+extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
+                                           const int8_t* q_codes, const int8_t* k_cache,
+                                           int32_t* dots, int64_t ld, void* stream) {
+  return indexer_common(batch, H, D, DSA_I8, DSA_F32, q_codes, nullptr, nullptr, k_cache, nullptr,
+                        nullptr, dots, true, ld, stream, "dsa_indexer_dots_i32");
+}

@@ -1,0 +1,194 @@
+"""Helpers for the GPU parity tests: upload a workload, run each stage through the C ABI,
+run the oracle on the same seeded inputs, and apply the comparison rules.
+
+Rules (the first three are the stated correctness bar; the others are diagnostics):
+  * int32 indexer dots: bit-exact.
+  * top-k: the GPU and oracle index sets may differ only by positions whose oracle score is
+    within 1e-5 * max(|I_k|, 1e-30) of the k-th oracle score I_k; the GPU set has k_eff
+    distinct positions in [0, p_t], ascending, then -1.
+  * attention output (bf16): max |delta| <= 1e-2 and mean |delta| <= 1e-3 against the float64
+    oracle.
+  * fp32 scores: |delta| <= 1e-5 * max_s |I[t, s]| (int8) -- rounding of 64 fp32 FMAs.
+  * prolog codes/scales: equal (both sides take the quantization decision in fp32 from the
+    same fp32 value; RoPE/Hadamard run in fp64 on both sides and are rounded once).
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from oracle.formats import bf16_decode
+from oracle.step import prolog_inputs_f64
+from sparse_attention_14_amd import dsa
+from sparse_attention_14_amd.step import IndexerCfg
+
+TOPK_REL = 1e-5
+SFA_MAX_ABS, SFA_MEAN_ABS = 1e-2, 1e-3
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def cfg_of(wl) -> IndexerCfg:
+    sp = wl.spec
+    return IndexerCfg(H=sp.H, D=sp.D, code=sp.code, scale_dt=sp.scale_dt,
+                      rope_dim=sp.rope_dim if sp.full_prolog else 0, rope_offset=sp.rope_offset,
+                      rope_interleaved=sp.rope_interleaved, hadamard=sp.full_prolog, k=sp.k)
+
+
+class Gpu:
+    """Device copy of a workload plus the GPU-quantized indexer operands."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self.d = workloads.device_arrays(wl)
+        self.batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start)
+        self.cfg = cfg_of(wl)
+        c = self.cfg
+        ct = torch.int8 if c.code == "i8" else torch.uint8
+        st = torch.float16 if c.scale_dt == "f16" else torch.float32
+        N, T = wl.N, wl.T
+        self.k_cache = torch.empty((N, c.D), dtype=ct, device="cuda")
+        self.k_scale = torch.empty((N,), dtype=st, device="cuda")
+        self.q_codes = torch.empty((T, c.H, c.D), dtype=ct, device="cuda")
+        self.q_scale = torch.empty((T, c.H), dtype=st, device="cuda")
+        d = self.d
+        dsa.dsa_indexer_prolog(c.H, c.D, c.code, c.scale_dt, q_in=d["idx_q_in"], q_cos=d["q_cos"],
+                               q_sin=d["q_sin"], q_codes=self.q_codes, q_scale=self.q_scale,
+                               k_in=d["idx_k_in"], k_cos=d["k_cos"], k_sin=d["k_sin"],
+                               k_slot=d["all_rows"], k_cache=self.k_cache, k_scale=self.k_scale,
+                               rope_dim=c.rope_dim, rope_offset=c.rope_offset,
+                               rope_interleaved=c.rope_interleaved, hadamard=c.hadamard)
+
+    def scores(self):
+        c = self.cfg
+        return dsa.dsa_indexer_scores(self.batch, c.H, c.D, c.code, c.scale_dt, self.q_codes,
+                                      self.q_scale, self.d["w"], self.k_cache, self.k_scale)
+
+    def topk(self, scores):
+        return dsa.dsa_topk(self.batch, scores, self.cfg.k)
+
+    def sfa(self, idx, sink=True):
+        d = self.d
+        return dsa.dsa_sparse_attn_decode(self.batch, d["q"], d["kv"], idx,
+                                          d["sink"] if sink else None, self.wl.scale)
+
+
+def codes_np(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def scales_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_quant(wl):
+    return oracle.step.quantize_workload(wl)
+
+
+def check_prolog(g: Gpu, oq) -> None:
+    cq, ck = codes_np(g.q_codes), codes_np(g.k_cache)
+    if g.cfg.code == "i8":
+        cq, ck = cq.astype(np.int8), ck.astype(np.int8)
+    nq = int(np.sum(cq != oq["q_codes"]))
+    nk = int(np.sum(ck != oq["k_codes"]))
+    sq = int(np.sum(scales_f64(g.q_scale) != oq["q_scale"]))
+    sk = int(np.sum(scales_f64(g.k_scale) != oq["k_scale"]))
+    log(f"  prolog mismatches: q codes {nq}/{cq.size}, k codes {nk}/{ck.size}, "
+        f"q scales {sq}, k scales {sk}")
+    assert nq == 0 and nk == 0 and sq == 0 and sk == 0
+
+
+def check_scores(gs: torch.Tensor, os_rows, q_pos) -> float:
+    g = gs.cpu().numpy()
+    worst = 0.0
+    for t, o in enumerate(os_rows):
+        n = int(q_pos[t]) + 1
+        ref = np.max(np.abs(o)) if o.size else 0.0
+        err = np.max(np.abs(g[t, :n].astype(np.float64) - o)) if n else 0.0
+        rel = err / max(ref, 1e-30)
+        worst = max(worst, rel)
+    log(f"  scores: worst |dI| / max|I| = {worst:.3e}")
+    assert worst <= 1e-5
+    return worst
+
+
+def check_topk(gi: torch.Tensor, oi: np.ndarray, os_rows, q_pos, k: int) -> int:
+    g = gi.cpu().numpy()
+    diffs = 0
+    for t in range(g.shape[0]):
+        p = int(q_pos[t])
+        keff = min(k, p + 1)
+        row = g[t]
+        assert np.all(row[keff:] == -1), f"token {t}: padding"
+        sel = row[:keff]
+        assert np.all(np.diff(sel) > 0), f"token {t}: not strictly ascending"
+        assert sel.min() >= 0 and sel.max() <= p, f"token {t}: out of range"
+        a, b = set(sel.tolist()), set(oi[t, :keff].tolist())
+        sd = a ^ b
+        if sd:
+            Ik = oracle.topk.kth_score(os_rows[t], k)
+            tol = TOPK_REL * max(abs(Ik), 1e-30)
+            bad = [s for s in sd if abs(os_rows[t][s] - Ik) > tol]
+            assert not bad, f"token {t}: {len(bad)} differing positions beyond tolerance"
+            diffs += len(sd) // 2
+    log(f"  top-k: sets equal up to {diffs} near-tie swaps")
+    return diffs
+
+
+def sfa_errors(gout: torch.Tensor, oout: np.ndarray, tokens=None):
+    g = gout.float().cpu().numpy().astype(np.float64)
+    if tokens is not None:
+        g, oout = g[tokens], oout[tokens]
+    d = np.abs(g - oout)
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def check_sfa(gout, oout, tokens=None, what="attention") -> None:
+    mx, mn = sfa_errors(gout, oout, tokens)
+    log(f"  {what}: max|d| = {mx:.3e}, mean|d| = {mn:.3e}")
+    assert mx <= SFA_MAX_ABS and mn <= SFA_MEAN_ABS
+
+
+def run_e2e(wl, token_subset=None, check_dots=False):
+    """Full GPU step vs oracle on the same inputs; token_subset restricts the oracle's work."""
+    log(f"case {wl.spec.name}: T={wl.T} B={wl.B} N={wl.N} H={wl.spec.H} D={wl.spec.D} "
+        f"code={wl.spec.code} k={wl.spec.k} Hq={wl.spec.Hq}")
+    g = Gpu(wl)
+    torch.cuda.synchronize()
+    log("  prolog done on GPU")
+    oq = oracle_quant(wl)
+    check_prolog(g, oq)
+    sc = g.scores()
+    idx = g.topk(sc)
+    out = g.sfa(idx)
+    torch.cuda.synchronize()
+    log("  GPU step done")
+    toks = np.arange(wl.T) if token_subset is None else np.asarray(token_subset)
+    sp = wl.spec
+    os_rows = oracle.indexer_scores(oq["q_codes"][toks], oq["q_scale"][toks], wl.w[toks], oq["k_codes"],
+                                    oq["k_scale"], sp.code, wl.q_seq[toks], wl.q_pos[toks], wl.kv_start)
+    check_scores(sc[torch.as_tensor(toks, device="cuda")], os_rows, wl.q_pos[toks])
+    oi = oracle.topk_select(os_rows, sp.k)
+    check_topk(idx[torch.as_tensor(toks, device="cuda")], oi, os_rows, wl.q_pos[toks], sp.k)
+    oo = oracle.sparse_attention(wl.q[toks], wl.kv, oi, wl.q_seq[toks], wl.kv_start, wl.sink, wl.scale)
+    gsel = idx.cpu().numpy()[toks]
+    same = [i for i in range(len(toks)) if np.array_equal(gsel[i], oi[i])]
+    log(f"  {len(same)}/{len(toks)} tokens with identical selections")
+    check_sfa(out[torch.as_tensor(toks, device="cuda")], oo, tokens=same, what="end-to-end attention")
+    if check_dots and sp.code == "i8":
+        dots = dsa.dsa_indexer_dots_i32(g.batch, sp.H, sp.D, g.q_codes, g.k_cache).cpu().numpy()
+        od = oracle.indexer_dots(oq["q_codes"][toks], oq["k_codes"], "i8", wl.q_seq[toks],
+                                 wl.q_pos[toks], wl.kv_start)
+        for i, t in enumerate(toks):
+            n = int(wl.q_pos[t]) + 1
+            assert np.array_equal(dots[t][:, :n].astype(np.int64), od[i].astype(np.int64)), f"dots token {t}"
+        log("  int32 dots bit-exact")
+    return g, sc, idx, out

@@ -1,0 +1,112 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments (or no-ops on empty batches) before making any HIP call -- no GPU needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _lib():
+    from sparse_attention_14_amd import _lib
+    return _lib
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return {m.group(1): m.group(2) for m in re.finditer(r"\b(dsa_\w+)\s*\(([^;{]*)\)\s*;", txt)}
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    decl = _declared()
+    assert {"dsa_indexer_prolog", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn_decode"} <= set(decl)
+    for name in decl:
+        assert hasattr(L.lib, name), name
+    out = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    for name in decl:
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported"
+
+
+def test_ctypes_signatures_match_header_arity():
+    L = _lib()
+    decl = _declared()
+    assert set(decl) == set(L.SIGNATURES)
+    for name, args in decl.items():
+        n = 0 if args.strip() in ("", "void") else args.count(",") + 1
+        assert n == len(L.SIGNATURES[name][1]), name
+
+
+def test_version_and_error_text():
+    L = _lib()
+    assert b"gfx950" in L.lib.dsa_version()
+    assert isinstance(L.lib.dsa_last_error(), bytes)
+
+
+def _batch(T=8, B=4, mq=2, ml=65536):
+    L = _lib()
+    p = ctypes.c_void_p(0x1000)          # never dereferenced: validation returns first
+    return L.DsaBatch(B, T, mq, ml, p, p, p, p)
+
+
+def test_validation_errors_before_any_device_call():
+    L = _lib()
+    lib = L.lib
+    b = _batch()
+    P = ctypes.c_void_p(0x1000)
+    # NULL batch
+    assert lib.dsa_indexer_scores(None, 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    assert b"batch is NULL" in lib.dsa_last_error()
+    # unsupported head shape
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 32, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, None) == L.DSA_ERR_UNSUPPORTED
+    # ld too small
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 100, None) == L.DSA_ERR_INVALID_ARG
+    # null data pointer
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, P, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    # top-k: k out of range, workspace too small
+    assert lib.dsa_topk(ctypes.byref(b), P, 65536, 4096, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(ctypes.byref(b), P, 65536, 2048, P, P, 16, None) == L.DSA_ERR_WORKSPACE
+    # sparse attention: unsupported heads, bad stride, missing workspace
+    assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 64, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 500, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 576, P, 2048, None, ctypes.c_float(-1.0), P, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    # prolog: bad D, bad rope range, missing pointers
+    cfg = L.DsaPrologCfg(64, 96, 0, 0, 0, 0, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, None, None, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_UNSUPPORTED
+    cfg = L.DsaPrologCfg(64, 128, 64, 96, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, P, P, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
+    cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, None, None, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
+
+
+def test_empty_batches_are_noops_without_device():
+    L = _lib()
+    lib = L.lib
+    b = _batch(T=0, B=0, mq=0, ml=0)
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, None) == L.DSA_OK
+    assert lib.dsa_topk(ctypes.byref(b), None, 0, 2048, None, None, 0, None) == L.DSA_OK
+    assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, None, None, 576, None, 2048, None, ctypes.c_float(0.04), None, None, 0, None) == L.DSA_OK
+    cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_FP8_E4M3, L.DSA_F16)
+    assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 0, None, None, None, None, None, 0, None, None, None, None, None, None, None) == L.DSA_OK
+    assert lib.dsa_topk_workspace_size(0, 10, 5) == 0 and lib.dsa_sparse_attn_workspace_size(0, 128, 5) == 0
+
+
+def test_workspace_sizes():
+    L = _lib()
+    # decode at 8 tokens spreads each token's 2048 keys over several workgroups
+    assert L.lib.dsa_sparse_attn_workspace_size(8, 128, 2048) > 0
+    # a large batch needs no split partials
+    assert L.lib.dsa_sparse_attn_workspace_size(4096, 128, 2048) == 0
+    assert L.lib.dsa_topk_workspace_size(8, 65536, 2048) >= 8 * 65536 * 8
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    from sparse_attention_14_amd import dsa
+    with pytest.raises(ValueError):
+        dsa._need(torch.zeros(3), "x", torch.float32)

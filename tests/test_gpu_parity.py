@@ -1,0 +1,187 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same seeded inputs.
+
+Small cases span several tiles with ragged tails and hit each edge the method has (short rows
+with -1 padding, exact ties, empty selections, no sink, fp8 with RoPE+Hadamard, many tokens
+per sequence); the named full-size workloads run the launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Spec, make
+from sparse_attention_14_amd import dsa
+
+from gpu_common import (Gpu, check_prolog, check_scores, check_sfa, check_topk, log, oracle_quant,
+                        run_e2e)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "ragged_i8": Spec("small_ragged_i8", 7001, [5000, 777, 3001], [2, 1, 3], k=512, Hq=128),
+    "short_rows": Spec("small_short_rows", 7002, [100, 3000, 256], [1, 1, 2], H=8, D=64,
+                       scale_dt="f32", k=256, Hq=16),
+    "fp8_prolog": Spec("small_fp8_prolog", 7003, [3000, 4500], [1, 2], code="e4m3",
+                       full_prolog=True, k=512, Hq=128),
+    "i8_prolog_interleaved": Spec("small_i8_prolog_il", 7004, [2000, 2100], [2, 2], full_prolog=True,
+                                  rope_interleaved=True, k=300, Hq=16),
+    "no_sink": Spec("small_no_sink", 7006, [2500], [1], k=2048, Hq=128, sink=False),
+    "many_tokens": Spec("small_many_tokens", 7005, [4096, 4096], [128, 128], k=256, Hq=128),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_end_to_end(name):
+    run_e2e(make(SMALL[name]), check_dots=True)
+
+
+def test_prolog_round_scale_and_scale_dtypes(rng):
+    for code in ("i8", "e4m3"):
+        for sdt in ("f16", "f32"):
+            sp = Spec(f"prolog_{code}_{sdt}", 7100, [700, 1300], [3, 1], code=code, scale_dt=sdt,
+                      full_prolog=True, k=64, Hq=16)
+            wl = make(sp)
+            log(f"case prolog {code}/{sdt} round_scale")
+            d = workloads.device_arrays(wl)
+            ct = torch.int8 if code == "i8" else torch.uint8
+            st = torch.float16 if sdt == "f16" else torch.float32
+            kc = torch.empty((wl.N, 128), dtype=ct, device="cuda")
+            ks = torch.empty((wl.N,), dtype=st, device="cuda")
+            dsa.dsa_indexer_prolog(64, 128, code, sdt, k_in=d["idx_k_in"], k_cos=d["k_cos"],
+                                   k_sin=d["k_sin"], k_slot=d["all_rows"], k_cache=kc, k_scale=ks,
+                                   rope_dim=64, rope_offset=64, hadamard=True, round_scale=True)
+            kin = oracle.formats.bf16_decode(wl.idx_k_in).astype(np.float32)
+            c, s, _ = oracle.prolog_rows(kin, wl.k_cos, wl.k_sin, 64, 64, False, True, code, sdt,
+                                         round_scale=True)
+            got = kc.cpu().numpy()
+            assert np.array_equal(got.astype(c.dtype), c)
+            assert np.array_equal(ks.float().cpu().numpy().astype(np.float64), s)
+
+
+def test_prolog_zero_rows_and_slots():
+    """All-zero rows quantize to zero codes and scale 0; rows land in their slots only."""
+    N, D = 64, 128
+    k_in = torch.zeros((4, D), dtype=torch.float32, device="cuda")
+    k_in[1] = torch.linspace(-3, 3, D, device="cuda")
+    kc = torch.full((N, D), 99, dtype=torch.int8, device="cuda")
+    ks = torch.full((N,), 7.0, dtype=torch.float16, device="cuda")
+    slots = torch.tensor([5, 17, 40, 63], dtype=torch.int64, device="cuda")
+    dsa.dsa_indexer_prolog(1, D, "i8", "f16", k_in=k_in, k_slot=slots, k_cache=kc, k_scale=ks)
+    kc_h, ks_h = kc.cpu().numpy(), ks.float().cpu().numpy()
+    for r, s in enumerate([5, 17, 40, 63]):
+        if r == 1:
+            c, st, _ = oracle.quantize_rows(k_in[1:2].cpu().numpy(), "i8", "f16")
+            assert np.array_equal(kc_h[s], c[0]) and ks_h[s] == st[0]
+        else:
+            assert not kc_h[s].any() and ks_h[s] == 0.0
+    untouched = np.setdiff1d(np.arange(N), [5, 17, 40, 63])
+    assert np.all(kc_h[untouched] == 99) and np.all(ks_h[untouched] == 7.0)
+
+
+def _topk_case(rng, T, L, k, kind):
+    if kind == "random":
+        s = rng.standard_normal((T, L)).astype(np.float32)
+    elif kind == "ties":          # few distinct values: many exact ties at the threshold
+        s = rng.integers(-3, 4, (T, L)).astype(np.float32)
+    elif kind == "zeros":         # +0 and -0 only
+        s = np.where(rng.random((T, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    else:                         # narrow band: candidates crowd the threshold digit
+        s = (1000.0 + rng.random((T, L)) * 1e-3).astype(np.float32)
+    return s
+
+
+@pytest.mark.parametrize("kind", ["random", "ties", "zeros", "narrow"])
+def test_topk_exact_on_identical_scores(rng, kind):
+    """Same fp32 scores on both sides: the selected sets must be identical (ties -> lower
+    positions), for long rows, rows shorter than k and rows of exactly k."""
+    lens = [70000, 2048, 2047, 100, 40000, 2049]
+    T, k = len(lens), 2048
+    L = max(lens)
+    s = _topk_case(rng, T, L, k, kind)
+    ld = (L + 63) // 64 * 64
+    sc = np.zeros((T, ld), dtype=np.float32)
+    sc[:, :L] = s
+    batch = dsa.make_batch(np.arange(T + 1), np.arange(T), np.array(lens) - 1, np.zeros(T))
+    log(f"case topk {kind}")
+    idx = dsa.dsa_topk(batch, torch.from_numpy(sc).cuda(), k).cpu().numpy()
+    rows = [sc[t, :lens[t]].astype(np.float64) for t in range(T)]
+    ref = oracle.topk_select(rows, k)
+    assert np.array_equal(idx, ref)
+
+
+def test_topk_all_zero_weights_select_first_positions():
+    sp = Spec("ties_w0", 7200, [9000, 3000], [1, 1], k=1024, Hq=16)
+    wl = make(sp)
+    wl.w[:] = 0
+    g = Gpu(wl)
+    idx = g.topk(g.scores()).cpu().numpy()
+    assert np.array_equal(idx[:, :1024], np.tile(np.arange(1024), (2, 1)))
+
+
+@pytest.mark.parametrize("Hq,T,sink,pad", [(128, 3, True, 0.0), (128, 5, False, 0.3),
+                                            (16, 2, True, 0.5), (128, 300, True, 0.1),
+                                            (16, 40, False, 0.0)])
+def test_sparse_attention_isolated(rng, Hq, T, sink, pad):
+    """Random selections (with -1 holes) straight into the attention kernel."""
+    lens = list(rng.integers(1500, 6000, size=T))
+    sp = Spec(f"sfa_{Hq}_{T}", 7300 + T, lens, [1] * T, H=8, D=64, k=2048, Hq=Hq, sink=sink)
+    wl = make(sp)
+    idx = workloads.random_topk_idx(rng, wl.q_pos, 2048, pad_frac=pad)
+    if T >= 3:
+        idx[1, :] = -1                                   # a token with an empty selection
+    log(f"case sfa Hq={Hq} T={T} sink={sink} pad={pad}")
+    d = workloads.device_arrays(wl)
+    batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start)
+    out = dsa.dsa_sparse_attn_decode(batch, d["q"], d["kv"], torch.from_numpy(idx).cuda(),
+                                     d["sink"] if sink else None, wl.scale)
+    ref = oracle.sparse_attention(wl.q, wl.kv, idx, wl.q_seq, wl.kv_start, wl.sink, wl.scale)
+    check_sfa(out, ref)
+    if T >= 3:
+        assert not out[1].float().abs().sum().item()
+
+
+def test_sparse_attention_strided_kv(rng):
+    """kv rows with a stride larger than 576 (e.g. a wider cache row)."""
+    sp = Spec("sfa_stride", 7400, [3000, 2500], [1, 1], H=8, D=64, k=1000, Hq=128)
+    wl = make(sp)
+    idx = workloads.random_topk_idx(rng, wl.q_pos, 1000)
+    kv_wide = torch.zeros((wl.N, 640), dtype=torch.bfloat16, device="cuda")
+    kv_wide[:, :576] = torch.from_numpy(wl.kv).view(torch.bfloat16).cuda()
+    d = workloads.device_arrays(wl)
+    batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start)
+    out = dsa.dsa_sparse_attn_decode(batch, d["q"], kv_wide[:, :576], torch.from_numpy(idx).cuda(),
+                                     d["sink"], wl.scale)
+    ref = oracle.sparse_attention(wl.q, wl.kv, idx, wl.q_seq, wl.kv_start, wl.sink, wl.scale)
+    check_sfa(out, ref)
+
+
+def test_empty_batch_noop():
+    batch = dsa.make_batch([0], [], [], [])
+    z = torch.zeros(0, device="cuda")
+    assert batch.num_q == 0
+    lib = dsa.lib
+    b = batch.c()
+    import ctypes
+    assert lib.dsa_topk(ctypes.byref(b), None, 0, 2048, None, None, 0, None) == 0
+    del z
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 4])
+def test_named_workload_end_to_end(cfg_id):
+    run_e2e(workloads.named(cfg_id), check_dots=(cfg_id == 1))
+
+
+def test_named_prefill_sampled_tokens():
+    """Prefill chunk (4096 new tokens on a 61440-token cache): the full GPU step, compared with
+    the oracle on sampled tokens (first, last, and seeded random ones)."""
+    wl = workloads.named(3)
+    rng = np.random.default_rng(31)
+    toks = np.unique(np.concatenate([[0, 1, 2047, 4095], rng.integers(0, 4096, 4)]))
+    run_e2e(wl, token_subset=toks)

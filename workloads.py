@@ -196,3 +196,28 @@ def random_topk_idx(rng: np.random.Generator, q_pos: np.ndarray, k: int,
             drop = rng.random(k) < pad_frac
             out[t, drop] = -1
     return out
+
+
+def device_arrays(wl: Workload, device="cuda") -> dict:
+    """The same workload as torch tensors on `device` (no arithmetic: copies and dtype views)."""
+    import torch
+
+    def dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(device)
+
+    in_t = torch.bfloat16 if wl.in_dtype == "bf16" else None
+    out = {
+        "q_start": dev(wl.q_start), "q_seq": dev(wl.q_seq), "q_pos": dev(wl.q_pos),
+        "kv_start": dev(wl.kv_start),
+        "idx_q_in": dev(wl.idx_q_in, in_t), "idx_k_in": dev(wl.idx_k_in, in_t),
+        "w": dev(wl.w), "kv": dev(wl.kv, torch.bfloat16), "q": dev(wl.q, torch.bfloat16),
+        "sink": None if wl.sink is None else dev(wl.sink),
+        "new_rows": dev(wl.new_rows()), "all_rows": torch.arange(wl.N, dtype=torch.int64, device=device),
+    }
+    for name in ("q_cos", "q_sin", "k_cos", "k_sin"):
+        v = getattr(wl, name)
+        out[name] = None if v is None else dev(v)
+    return out
