@@ -124,7 +124,8 @@ dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg,
  *   I[t,s]   = sum_h w[t,h] * ReLU(q_scale[t,h] * k_scale[s] * D[t,h,s]),   s = 0 .. p_t
  * evaluated as k_scale[s] * sum_h (w*q_scale)[t,h] * max(D[t,h,s], 0) in fp32 (the scales are
  * positive).  Supported: (H, D) in {(64,128), (8,64)}; codes DSA_I8 (int8 MFMA) or
- * DSA_FP8_E4M3 (fp8 MFMA); scales DSA_F16 or DSA_F32; w is fp16.
+ * DSA_FP8_E4M3 (codes widened exactly to bf16, bf16 MFMA, fp32 sums); scales DSA_F16 or
+ * DSA_F32; w is fp16.
  *   q_codes  device [T, H, D]          q_scale device [T, H]        w device [T, H] fp16
  *   k_cache  device [N, D] (rows of every sequence, see dsa_batch)  k_scale device [N]
  *   scores   device [T, ld] fp32, ld >= max_kv_len, ld % 4 == 0.  Row t gets columns 0 .. p_t;
@@ -154,7 +155,10 @@ dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
  * order-preserving keys; -0.0 equals +0.0).  1 <= k <= 2048.
  *   scores device [T, ld] fp32 (as written by dsa_indexer_scores), idx device [T, k] int32.
  *   ws: device workspace of at least dsa_topk_workspace_size(T, max_kv_len, k) bytes,
- *       256-byte aligned; contents need no initialisation and are scratch afterwards.
+ *       256-byte aligned, ZERO-FILLED before its first use; every call leaves it zero-filled
+ *       again (it holds per-row histograms and completion counters), so a workspace is
+ *       allocated and cleared once and then reused.  Calls sharing a workspace must not
+ *       overlap.  max_kv_len <= 262144.
  */
 size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k);
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,

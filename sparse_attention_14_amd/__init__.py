@@ -3,13 +3,22 @@
     from sparse_attention_14_amd import dsa            # the binding (same names as dsa.h)
     from sparse_attention_14_amd.step import decode_step
 
-Importing fails loudly if libdsa.so has not been built; there is no fallback path.
+The binding loads libdsa.so when it is first used and raises ImportError if the library has
+not been built (python -m sparse_attention_14_amd.build); there is no fallback path.  The
+package itself imports without the library so that the build module can run.
 """
-from . import dsa  # noqa: F401  (loads libdsa.so)
-from .dsa import (Batch, make_batch, dsa_indexer_prolog, dsa_indexer_scores, dsa_indexer_dots_i32,
-                  dsa_topk, dsa_topk_workspace_size, dsa_sparse_attn_decode,
-                  dsa_sparse_attn_workspace_size, dsa_last_error, dsa_version)
+import importlib
 
-__all__ = ["dsa", "Batch", "make_batch", "dsa_indexer_prolog", "dsa_indexer_scores",
-           "dsa_indexer_dots_i32", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_decode",
-           "dsa_sparse_attn_workspace_size", "dsa_last_error", "dsa_version"]
+_EXPORTS = ("Batch", "make_batch", "dsa_indexer_prolog", "dsa_indexer_scores",
+            "dsa_indexer_dots_i32", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_decode",
+            "dsa_sparse_attn_workspace_size", "dsa_last_error", "dsa_version")
+
+__all__ = ["dsa", *_EXPORTS]
+
+
+def __getattr__(name):
+    if name == "dsa":
+        return importlib.import_module(".dsa", __name__)
+    if name in _EXPORTS:
+        return getattr(importlib.import_module(".dsa", __name__), name)
+    raise AttributeError(name)

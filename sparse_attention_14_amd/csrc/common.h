@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 
 namespace dsa {
 
@@ -37,6 +37,12 @@ __device__ __forceinline__ float f16_bits_to_f32(u16 h) {
 __device__ __forceinline__ u16 f32_to_f16_bits(float f) {
   return __builtin_bit_cast(u16, static_cast<_Float16>(f));
 }
+
+// Make the compiler retire the load that produced `v` here (an empty asm that reads the
+// register): used before a stream of loads issued from inline asm, so that the compiler's own
+// later waits for such a register cannot also drain the asm-issued loads it cannot count.
+template <typename T>
+__device__ __forceinline__ void retire(const T& v) { asm volatile("" :: "v"(v)); }
 
 // Flat workgroup id remapped so that consecutive logical ids land on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); logical id

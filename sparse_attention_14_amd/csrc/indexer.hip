@@ -93,10 +93,39 @@ __device__ __forceinline__ typename AccT<FP8>::type mma_block(const KFrag<FP8, D
   return c;
 }
 
+// Key chunk staging.  The chunk's key rows (CK x D bytes) and its key scales are moved
+// HBM -> LDS with global_load_lds_dwordx4 issued from inline asm (each lane's 16 bytes land
+// at M0 + 16 * lane), all at once, in four groups of 128 keys that are consumed as they land
+// (explicit s_waitcnt vmcnt).  The compiler neither sees these loads (so it does not drain
+// them at every LDS read) nor can sink them.  Inside the key loop no other vector-memory
+// operation is issued -- scores go to LDS and are stored once at the end -- so the manual
+// vmcnt values are exact.  Row r's 16-byte chunk c sits at chunk c ^ (r % CPR): 16-byte
+// reads of one chunk column by 32 consecutive rows spread over all banks.
+__device__ __forceinline__ void idx_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void idx_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// 16 bytes at base + off (base wave-uniform in SGPRs) into LDS at lds_addr + 16 * lane
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, unsigned lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(lds_addr));
+}
+
+constexpr int kGroups = 4;                    // 128-key groups per chunk
+
 // G = query tokens per workgroup (1, 2, 4); NMB = 32-head M-blocks per token (ceil(H/32)).
-template <int G, int NMB, int D, bool FP8, bool DOTS>
+template <int G, int NMB, int D, bool FP8, bool DOTS, bool SF16>
 __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   constexpr int NPH = 4 / G;                 // waves sharing one token
+  constexpr int CPR = D / 16;                // 16-byte chunks per key row
+  constexpr int KB = kCK * D;                // chunk bytes in LDS
+  constexpr int INSTR = KB / 1024;           // DMA wave-instructions for the chunk
+  constexpr int PER_GROUP = INSTR / 4 / kGroups;   // per thread per group
+  __shared__ __attribute__((aligned(1024))) unsigned char kl[KB];
+  __shared__ float scl[DOTS ? 1 : G][kCK];                              // scores of the chunk
+
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hv = lane >> 5, col = lane & 31;
   const int b = blockIdx.y / a.ngrp, g = blockIdx.y % a.ngrp;
@@ -108,24 +137,22 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
   const int chunk0 = blockIdx.x * kCK;
   if (chunk0 > maxp) return;
-  const int t = q_lo + wave % G;
-  if (t >= q_hi) return;
+  const int ti = wave % G;                   // this wave's token
+  const int t = q_lo + ti;
+  const bool live = t < q_hi;
   const int phase = wave / G;
-  const int p = a.q_pos[t];
+  const int p = live ? a.q_pos[t] : -1;
   const long kv0 = a.kv_start[b];
   const int H = a.H;
 
-  // query codes of token t: M-block mb, row col -> head 32 mb + col
+  // Loads below are unconditional (clamped indices, results selected afterwards): a load
+  // behind a per-element branch is issued and waited for one at a time.
+  const int tc = live ? t : q_hi - 1;
   KFrag<FP8, D> qf[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
-    const int h = 32 * mb + col;
-    if (h < H) {
-      load_row_half<FP8, D>(qf[mb], a.q_codes + ((long)t * H + h) * D + hv * (D / 2));
-    } else {
-#pragma unroll
-      for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[mb].v[j] = {};
-    }
+    const int h = min(32 * mb + col, H - 1);
+    load_row_half<FP8, D>(qf[mb], a.q_codes + ((long)tc * H + h) * D + hv * (D / 2));
   }
   // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane
   float wq[NMB][16];
@@ -135,61 +162,143 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
-        float v = 0.f;
-        if (h < H) {
-          const long o = (long)t * H + h;
-          const float qs = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.q_scale)[o])
-                                       : ((const float*)a.q_scale)[o];
-          v = f16_bits_to_f32(a.w[o]) * qs;
-        }
-        wq[mb][i] = v;
+        const long o = (long)tc * H + min(h, H - 1);
+        const float qs = SF16 ? f16_bits_to_f32(((const u16*)a.q_scale)[o]) : ((const float*)a.q_scale)[o];
+        const float v = f16_bits_to_f32(a.w[o]) * qs;
+        wq[mb][i] = (h < H) ? v : 0.f;
       }
   }
+  // query rows past H are zero (they pair with zero weights; their dots are not stored)
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+    if (32 * mb + col >= H) {
+#pragma unroll
+      for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[mb].v[j] = {};
+    }
+  // key scales of this lane's key in each block the wave will visit (row-clamped)
+  const int last_row = maxp - chunk0;        // rows past it are clamped (never stored)
+  constexpr int NBW = kCK / kBlk / NPH;      // blocks per wave
+  float ksr[DOTS ? 1 : NBW];
+  if constexpr (!DOTS) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int r = min((phase + NPH * j) * kBlk + col, last_row);
+      const long row = kv0 + chunk0 + r;
+      ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+    }
+  }
+  // retire every load above before the DMA stream starts
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) retire(qf[mb].v[j]);
+  if constexpr (!DOTS) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) retire(wq[mb][i]);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) retire(ksr[j]);
+  }
+  __syncthreads();
 
-  for (int kb = phase; kb < kCK / kBlk; kb += NPH) {
-    const int s0 = chunk0 + kb * kBlk;
-    if (s0 > p) break;
-    const int s = s0 + col;
-    const long row = kv0 + min(s, p);                     // clamp: stay inside the sequence
-    KFrag<FP8, D> kf;
-    load_row_half<FP8, D>(kf, a.k_cache + row * D + hv * (D / 2));
-    float ks = 0.f;
-    if constexpr (!DOTS)
-      ks = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
-    if constexpr (DOTS) {
+  // ---- DMA of the key rows, group by group
+  const unsigned kl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kl;
+  const uint8_t* kchunk = a.k_cache + (kv0 + chunk0) * D;   // wave-uniform DMA base
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const auto acc = mma_block<FP8, D>(qf[mb], kf);
-        if (s <= p) {
+  for (int it = 0; it < INSTR / 4; ++it) {
+    const int j = wave + 4 * it;
+    const int o = j * 1024 + lane * 16;
+    const int r = o / D;
+    const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
+    const int rr = min(r, last_row);
+    dma16(kchunk, (uint32_t)(rr * D + c * 16), kl_base + j * 1024);
+  }
+
+  // ---- consume the groups as they land
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
-            if (h < H) a.dots[((long)t * H + h) * a.ld + s] = (int32_t)acc[i];
+  for (int grp = 0; grp < kGroups; ++grp) {
+    if (grp == 0) idx_wait_vm<PER_GROUP * 3>();
+    else if (grp == 1) idx_wait_vm<PER_GROUP * 2>();
+    else if (grp == 2) idx_wait_vm<PER_GROUP * 1>();
+    else idx_wait_vm<0>();
+    idx_lds_barrier();
+    if (!live) continue;
+#pragma unroll
+    for (int kb = grp * (kCK / kBlk / kGroups) + phase; kb < (grp + 1) * (kCK / kBlk / kGroups); kb += NPH) {
+      const int sl0 = kb * kBlk;             // key row in the chunk
+      const int s = chunk0 + sl0 + col;
+      if (chunk0 + sl0 > p) break;
+      const int r = sl0 + col;
+      KFrag<FP8, D> kf;
+      {
+        // this lane's D/2 bytes: logical chunks hv*CPR/2 .. +CPR/2 of row r
+        v4i raw[CPR / 2];
+#pragma unroll
+        for (int q = 0; q < CPR / 2; ++q) {
+          const int cc = hv * (CPR / 2) + q;
+          raw[q] = *reinterpret_cast<const v4i*>(kl + r * D + ((cc ^ (r & (CPR - 1))) << 4));
+        }
+        if constexpr (!FP8) {
+#pragma unroll
+          for (int q = 0; q < CPR / 2; ++q) kf.v[q] = raw[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < CPR / 2; ++q) {
+            kf.v[2 * q] = fp8x8_to_bf16<D>(raw[q][0], raw[q][1]);
+            kf.v[2 * q + 1] = fp8x8_to_bf16<D>(raw[q][2], raw[q][3]);
           }
         }
       }
-    } else {
-      float sum = 0.f;
+      if constexpr (DOTS) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const auto acc = mma_block<FP8, D>(qf[mb], kf);
+        for (int mb = 0; mb < NMB; ++mb) {
+          const auto acc = mma_block<FP8, D>(qf[mb], kf);
+          if (s <= p) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float d;
-          if constexpr (FP8) d = fmaxf(acc[i], 0.f);
-          else d = (float)max(acc[i], 0);
-          sum = fmaf(wq[mb][i], d, sum);
+            for (int i = 0; i < 16; ++i) {
+              const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
+              if (h < H) a.dots[((long)t * H + h) * a.ld + s] = (int32_t)acc[i];
+            }
+          }
         }
+      } else {
+        const float ks = ksr[(kb - phase) / NPH];
+        float sum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const auto acc = mma_block<FP8, D>(qf[mb], kf);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float d;
+            if constexpr (FP8) d = fmaxf(acc[i], 0.f);
+            else d = (float)max(acc[i], 0);
+            sum = fmaf(wq[mb][i], d, sum);
+          }
+        }
+        sum += __shfl_xor(sum, 32, kWave);
+        if (hv == 0) scl[ti][r] = sum * ks;
       }
-      sum += __shfl_xor(sum, 32, kWave);
-      if (hv == 0 && s <= p) a.scores[(long)t * a.ld + s] = sum * ks;
+    }
+  }
+  if constexpr (!DOTS) {
+    __syncthreads();
+    // coalesced score stores: token j of the group, keys chunk0 .. min(chunk0 + kCK, p_j + 1)
+    for (int j = 0; j < G; ++j) {
+      const int tj = q_lo + j;
+      if (tj >= q_hi) break;
+      const int pj = a.q_pos[tj];
+      const int n = min(kCK, pj + 1 - chunk0);
+      float* dst = a.scores + (long)tj * a.ld + chunk0;
+      for (int e = threadIdx.x; e < n; e += 256) dst[e] = scl[j][e];
     }
   }
 }
 
 template <int G, int NMB, int D, bool FP8, bool DOTS>
 static void launch(const IdxArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS>), grid, dim3(256), 0, st, a);
+  if (a.scale_f16) hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, false>), grid, dim3(256), 0, st, a);
 }
 
 template <int NMB, int D, bool FP8, bool DOTS>

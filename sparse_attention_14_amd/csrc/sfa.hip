@@ -28,9 +28,12 @@
 namespace dsa {
 
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kKT = 64;                              // keys per tile
-constexpr int kPitch = kDqk * 2 + 16;                // LDS row pitch in bytes (1168)
-constexpr int kChunks = kDqk * 2 / 16;               // 72 16-byte chunks per row
+constexpr int kKT = 32;                              // keys per tile
+constexpr int kRowB = kDqk * 2;                      // 1152 bytes per latent row
+constexpr int kTileB = kKT * kRowB;                  // 36864 bytes per tile
+constexpr int kPairLoads = 2 * kTileB / 16 / 512;    // 9 DMA loads per thread per tile pair
+constexpr int kNBuf = 4;                             // tiles in the LDS ring
+constexpr int kMaxKps = 2048;                        // keys per split (LDS index stage)
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -48,19 +51,166 @@ struct SfaArgs {
 
 __device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
 
-template <int NB, bool FINAL>
-__global__ void __launch_bounds__(256) sfa_kernel(SfaArgs a) {
-  constexpr int NH = 16 * NB;
-  constexpr int PP = 144;                            // P row pitch in bytes (64 keys + 16 B pad)
-  __shared__ __attribute__((aligned(16))) unsigned char kt[kKT * kPitch];
-  __shared__ __attribute__((aligned(16))) unsigned char pt[NH * PP];
+// Rows are stored unpadded (1152 B) with the 16-byte chunk c of row r at chunk c ^ (r & 7):
+// 16-byte reads of one logical chunk from 8 consecutive rows then fall in distinct banks.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
+
+// Pipeline control.  Tiles move HBM -> LDS with global_load_lds_dwordx4 (each lane's 16 bytes
+// land at M0 + 16 * lane), issued from inline asm together with explicit s_waitcnt vmcnt(N)
+// and an LDS-only barrier:
+//  * __syncthreads() also fences global memory and waits for every load in flight;
+//  * for a compiler-issued LDS DMA the compiler waits for all DMA traffic before any LDS
+//    read, as it cannot tell ring slots apart;
+// either would serialise the ring.  Inside the tile loop the only vector-memory operations
+// in flight are these tile loads, so vmcnt(N) with N = loads issued after tile i is exact.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+struct SfaState {
+  v4f acc_o[4][2];             // O^T[64-dim slice of this wave][32 heads]
+  float m_run[2], l_run[2];    // per head 16 nb + c16 (identical in every wave)
+};
+
+constexpr float kLazy = 8.f;   // log2-domain headroom before the running max is moved
+constexpr int kPP = 2 * kKT * 2 + 16;   // P row pitch: 64 keys (a tile pair) + 16 B pad
+
+// One tile pair (64 keys) on 8 waves.
+//  S^T = K Q^T : wave w takes tile 2k + (w>>2), keys 16 (w&1) .. +15, heads 16 ((w>>1)&1) .. +15
+//                (Q of its 16 heads stays in VGPRs as the MFMA B operand).
+//  softmax     : per-head pair max through LDS; the reference max m only moves when the pair's
+//                max exceeds it by more than kLazy, so P < 2^kLazy and the accumulators are
+//                rarely rescaled (the final normalisation uses the same m: exact).
+//  O^T += V^T P^T : wave w owns value dims 64 w .. +63 for all 32 heads over both tiles
+//                (V^T via ds_read_b64_tr_b16, P^T from LDS).
+__device__ __forceinline__ void pair_step(SfaState& st, const unsigned char* t0,
+                                          const unsigned char* t1, const v8bf* qf,
+                                          const int* sidx, int key0, int nkeys, float scale_log2,
+                                          unsigned char* pt, float (*red_max)[32],
+                                          float (*red_sum)[32]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int th = wave >> 2, kh = wave & 1, hb = (wave >> 1) & 1;
+  const int q4 = 2 * th + kh;                          // key quarter of the pair
+  const unsigned char* tile = th ? t1 : t0;
+  v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  {
+    const int r = 16 * kh + c16;
+    // K fragments are read two k-steps ahead of their MFMAs; the scheduling barriers keep the
+    // compiler from hoisting all 18 reads to the top.
+    v8bf a0 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, g));
+    v8bf a1 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 + g));
+#pragma unroll
+    for (int ks = 0; ks < 18; ks += 2) {
+      v8bf n0 = a0, n1 = a1;
+      if (ks + 2 < 18) {
+        n0 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 * ks + 8 + g));
+        n1 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 * ks + 12 + g));
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = n0; a1 = n1;
+    }
+  }
+  v4f s = s0 + s1;
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int key = key0 + 16 * q4 + 4 * g + e;
+    const float z = (key < nkeys && sidx[key] >= 0) ? s[e] * scale_log2 : -INFINITY;
+    s[e] = z;
+    m = fmaxf(m, z);
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  if (g == 0) red_max[q4][16 * hb + c16] = m;
+  lds_barrier();
+  float alpha[2], mnew[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int h = 16 * nb + c16;
+    const float tm = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
+    const float mo = st.m_run[nb];
+    const bool move = (mo == -INFINITY) ? (tm != -INFINITY) : (tm > mo + kLazy);
+    mnew[nb] = move ? tm : mo;
+    alpha[nb] = move ? ((mo == -INFINITY) ? 0.f : exp2f(mo - tm)) : 1.f;
+  }
+  {
+    const float mn = mnew[hb];
+    float ps = 0.f;
+    u16 pb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pv = mn == -INFINITY ? 0.f : exp2_or_zero(s[e] - mn);
+      pb[e] = f32_to_bf16(pv);
+      ps += bf16_to_f32(pb[e]);
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    const int h = 16 * hb + c16;
+    if (g == 0) red_sum[q4][h] = ps;
+    uint2 pk;
+    pk.x = (uint32_t)pb[0] | ((uint32_t)pb[1] << 16);
+    pk.y = (uint32_t)pb[2] | ((uint32_t)pb[3] << 16);
+    *reinterpret_cast<uint2*>(pt + h * kPP + (16 * q4 + 4 * g) * 2) = pk;
+  }
+  lds_barrier();
+  bool rescale = false;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int h = 16 * nb + c16;
+    st.l_run[nb] = alpha[nb] * st.l_run[nb] + (red_sum[0][h] + red_sum[1][h]) + (red_sum[2][h] + red_sum[3][h]);
+    st.m_run[nb] = mnew[nb];
+    rescale |= alpha[nb] != 1.f;
+  }
+  if (__any(rescale)) {                                // wave-uniform, rare after the first pair
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) { st.acc_o[mb][0] *= alpha[0]; st.acc_o[mb][1] *= alpha[1]; }
+  }
+  // V^T via ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 values of row
+  // kb + j/4, columns d0 + 4 (j%4) .. +3; lane i receives the 4 rows of column d0 + i.
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const lds_u8* tl = (const lds_u8*)(tt ? t1 : t0);
+    v8bf pf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      pf[nb] = *reinterpret_cast<const v8bf*>(pt + (16 * nb + c16) * kPP + (32 * tt + 8 * g) * 2);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int col = 64 * wave + 16 * mb + 4 * (c16 & 3);
+      const int r0 = 8 * g + (c16 >> 2), r1 = r0 + 4;
+      const int c = col >> 3, wi = (col & 7) * 2;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r0, c) + wi));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r1, c) + wi));
+      const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      st.acc_o[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], st.acc_o[mb][0], 0, 0, 0);
+      st.acc_o[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], st.acc_o[mb][1], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One workgroup (8 waves): token t, query heads h0 .. h0+31, selected keys [kbeg, kbeg+nkeys),
+// consumed as pairs of 32-key tiles.  Tiles flow HBM -> 4-slot LDS ring (the next pair in
+// flight while the current pair is consumed) -> MFMA; 8 waves give each SIMD two waves that
+// hide each other's latency.
+template <bool FINAL>
+__global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
+  constexpr int NH = 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kNBuf * kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char pt[NH * kPP];
   __shared__ float red_max[4][NH];
   __shared__ float red_sum[4][NH];
-  __shared__ long rows[kKT];
-  lds_u8* const kt_lds = (lds_u8*)kt;
+  __shared__ int sidx[kMaxKps];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int g = lane >> 4, c16 = lane & 15, hb = (wave >> 1) & 1;
   const int nwg = a.T * a.n_hg * a.n_split;
   const int lid = xcd_remap(blockIdx.x, nwg);
   const int hg = lid % a.n_hg;
@@ -68,205 +218,159 @@ __global__ void __launch_bounds__(256) sfa_kernel(SfaArgs a) {
   const int t = ts / a.n_split, split = ts % a.n_split;
   const int h0 = hg * NH;
   const int kbeg = split * a.kps;
-  const int kend = min(a.k, kbeg + a.kps);
+  const int nkeys = min(a.k, kbeg + a.kps) - kbeg;
   const long kv0 = a.kv_start[a.q_seq[t]];
+  const unsigned ring_base = (unsigned)(uintptr_t)(lds_u8*)ring;
+  // DMA addressing: a wave-uniform base (the sequence's first latent row, SGPRs) plus a
+  // 32-bit per-lane byte offset (the host checks that a sequence spans < 4 GiB)
+  const u16* kv_seq = a.kv + kv0 * a.kv_stride;
+  const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
 
-  // Q^T fragments: lane holds head h0 + 16 nb + c16, dims 32 ks + 8 g .. +7
-  v8bf qf[NB][18];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const u16* qrow = a.q + ((long)t * a.Hq + h0 + 16 * nb + c16) * kDqk + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[nb][ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
-  }
-
-  v4f acc_o[8][NB];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc_o[mb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run[NB], l_run[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) { m_run[nb] = -INFINITY; l_run[nb] = 0.f; }
-
-  for (int key0 = kbeg; key0 < kend; key0 += kKT) {
-    // ---- selected rows of this tile
-    if (tid < kKT) {
-      const int j = key0 + tid;
-      long r = -1;
-      if (j < kend) {
-        const int ix = a.idx[(long)t * a.k + j];
-        if (ix >= 0) r = kv0 + ix;
-      }
-      rows[tid] = r;
-    }
-    __syncthreads();
-    // ---- gather 64 x 1152 B into LDS; unused slots are zero-filled
-#pragma unroll 6
-    for (int it = 0; it < kKT * kChunks / 256; ++it) {
-      const int f = tid + 256 * it;
-      const int r = f / kChunks, c = f % kChunks;
-      const long row = rows[r];
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (row >= 0) v = *reinterpret_cast<const uint4*>(a.kv + row * a.kv_stride + c * 8);
-      *reinterpret_cast<uint4*>(kt + r * kPitch + c * 16) = v;
-    }
-    __syncthreads();
-
-    // ---- S^T = K . Q^T for keys 16 wave .. +15 of the tile
-    v4f s[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-    const unsigned char* arow = kt + (16 * wave + c16) * kPitch + 16 * g;
+  for (int j = tid; j < nkeys; j += 512) sidx[j] = a.idx[(long)t * a.k + kbeg + j];
+  v8bf qf[18];
+  {
+    const int hq = h0 + 16 * hb + c16;                 // heads past Hq (Hq = 16) stay zero
+    const u16* qrow = a.q + ((long)t * a.Hq + min(hq, a.Hq - 1)) * kDqk + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const v8bf af = *reinterpret_cast<const v8bf*>(arow + 64 * ks);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[nb][ks], s[nb], 0, 0, 0);
+      qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
+      if (hq >= a.Hq) qf[ks] = v8bf{};
     }
-    // lane holds keys 16 wave + 4 g + i (i < 4) of head h0 + 16 nb + c16
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = 16 * wave + 4 * g + i;
-        const float z = rows[slot] >= 0 ? s[nb][i] * a.scale_log2 : -INFINITY;
-        s[nb][i] = z;
-        m = fmaxf(m, z);
-      }
-      m = fmaxf(m, __shfl_xor(m, 16, kWave));
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      if (g == 0) red_max[wave][16 * nb + c16] = m;
-    }
-    __syncthreads();
-    float alpha[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int hl = 16 * nb + c16;
-      const float tm = fmaxf(fmaxf(red_max[0][hl], red_max[1][hl]), fmaxf(red_max[2][hl], red_max[3][hl]));
-      const float mn = fmaxf(m_run[nb], tm);
-      alpha[nb] = (m_run[nb] == -INFINITY) ? (mn == -INFINITY ? 1.f : 0.f) : exp2f(m_run[nb] - mn);
-      float ps = 0.f;
-      u16 pb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = mn == -INFINITY ? 0.f : exp2_or_zero(s[nb][i] - mn);
-        pb[i] = f32_to_bf16(pv);
-        ps += bf16_to_f32(pb[i]);
-      }
-      ps += __shfl_xor(ps, 16, kWave);
-      ps += __shfl_xor(ps, 32, kWave);
-      if (g == 0) red_sum[wave][hl] = ps;
-      uint2 pk;
-      pk.x = (uint32_t)pb[0] | ((uint32_t)pb[1] << 16);
-      pk.y = (uint32_t)pb[2] | ((uint32_t)pb[3] << 16);
-      *reinterpret_cast<uint2*>(pt + hl * PP + (16 * wave + 4 * g) * 2) = pk;
-      m_run[nb] = mn;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int hl = 16 * nb + c16;
-      l_run[nb] = alpha[nb] * l_run[nb] + (red_sum[0][hl] + red_sum[1][hl] + red_sum[2][hl] + red_sum[3][hl]);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc_o[mb][nb] *= alpha[nb];
-    }
-
-    // ---- O^T += V^T . P^T for value dims 128 wave .. +127
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8bf pf[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        pf[nb] = *reinterpret_cast<const v8bf*>(pt + (16 * nb + c16) * PP + (32 * ks + 8 * g) * 2);
-      // V^T fragment via LDS transpose reads: in each 16-lane group, lane j points at
-      // 4 values of row (kb + j/4), columns d0 + 4(j%4) .. +3; ds_read_b64_tr_b16 hands
-      // lane i the 4 rows of column d0 + i.  Two reads give keys kb .. kb+7.
-      const int kb = 32 * ks + 8 * g;
-      const int toff = (kb + (c16 >> 2)) * kPitch + (128 * wave + 4 * (c16 & 3)) * 2;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int o = toff + 32 * mb;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kt_lds + o));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kt_lds + o + 4 * kPitch));
-        const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc_o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc_o[mb][nb], 0, 0, 0);
-      }
-    }
-    __syncthreads();
   }
-
-  // ---- epilogue: lane holds O^T[d = 128 wave + 16 mb + 4 g + i][head h0 + 16 nb + c16]
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int ks = 0; ks < 18; ++ks) retire(qf[ks]);      // Q landed before the DMA stream
+  __syncthreads();                                     // indices visible
+
+  SfaState st;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) { st.acc_o[mb][0] = v4f{0.f, 0.f, 0.f, 0.f}; st.acc_o[mb][1] = st.acc_o[mb][0]; }
+  st.m_run[0] = st.m_run[1] = -INFINITY;
+  st.l_run[0] = st.l_run[1] = 0.f;
+
+  const int nt = (nkeys + kKT - 1) / kKT;
+  const int npairs = (nt + 1) / 2;
+  // a pair = tiles 2k, 2k+1 in ring slots (2k)%4, (2k+1)%4: 72 wave-instructions of 1 KiB,
+  // J = wave + 8 it (it < 9), so every thread issues exactly kPairLoads DMA loads per pair.
+  // A tile past nt (odd tile count) loads clamped, valid rows whose keys are masked.
+  auto issue_pair = [&](int k) {
+    // opaque lane id: keeps the per-load offsets from being hoisted out of the pair loop
+    // (hoisted, they do not fit the register budget and get spilled)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int it = 0; it < kPairLoads; ++it) {
+      const int J = wave + 8 * it;
+      const int half = J >= kTileB / 1024 ? 1 : 0;
+      const int j = J - half * (kTileB / 1024);
+      const int tl = 2 * k + half;
+      const int o = j * 1024 + ln * 16;
+      const int r = o / kRowB;
+      const int c = ((o % kRowB) >> 4) ^ (r & 7);
+      const int key = min(tl * kKT + r, nkeys - 1);
+      const int ix = max(sidx[key], 0);                // unused slot: any valid row (masked)
+      const uint32_t off = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(kv_seq),
+                   "{m0}"(ring_base + (tl % kNBuf) * kTileB + j * 1024));
+    }
+  };
+  if (npairs > 0) issue_pair(0);
+  for (int k = 0; k < npairs; ++k) {
+    lds_barrier();                                     // pair k-1 fully consumed (ring slots free)
+    if (k + 1 < npairs) { issue_pair(k + 1); wait_vm<kPairLoads>(); } else { wait_vm<0>(); }
+    lds_barrier();                                     // pair k landed for every thread
+    pair_step(st, ring + ((2 * k) % kNBuf) * kTileB, ring + ((2 * k + 1) % kNBuf) * kTileB, qf,
+              sidx, 2 * k * kKT, nkeys, a.scale_log2, pt, red_max, red_sum);
+  }
+  const int wave4 = wave;                              // value-dim slice (64 wide) of this wave
+
+  // ---- epilogue: lane holds O^T[d = 64 wave + 16 mb + 4 g + e][head h0 + 16 nb + c16]
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
     const int h = h0 + 16 * nb + c16;
+    if (h >= a.Hq) continue;
     if constexpr (FINAL) {
       const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-      const float M = fmaxf(m_run[nb], sk);
-      const float f = m_run[nb] == -INFINITY ? 0.f : exp2f(m_run[nb] - M);
-      const float den = l_run[nb] * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
+      const float M = fmaxf(st.m_run[nb], sk);
+      const float f = st.m_run[nb] == -INFINITY ? 0.f : exp2f(st.m_run[nb] - M);
+      const float den = st.l_run[nb] * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
       const float inv = den > 0.f ? f / den : 0.f;
-      u16* orow = a.out + ((long)t * a.Hq + h) * kDv + 128 * wave + 4 * g;
+      u16* orow = a.out + ((long)t * a.Hq + h) * kDv + 64 * wave4 + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc_o[mb][nb][0] * inv) | ((uint32_t)f32_to_bf16(acc_o[mb][nb][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc_o[mb][nb][2] * inv) | ((uint32_t)f32_to_bf16(acc_o[mb][nb][3] * inv) << 16);
+        pk.x = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][0] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][2] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][3] * inv) << 16);
         *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
       }
     } else {
       const long base = ((long)t * a.n_split + split) * a.Hq + h;
-      float* orow = a.ws_o + base * kDv + 128 * wave + 4 * g;
+      float* orow = a.ws_o + base * kDv + 64 * wave4 + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<v4f*>(orow + 16 * mb) = acc_o[mb][nb];
-      if (wave == 0 && g == 0) {
-        a.ws_ml[base * 2 + 0] = m_run[nb];
-        a.ws_ml[base * 2 + 1] = l_run[nb];
+      for (int mb = 0; mb < 4; ++mb) *reinterpret_cast<v4f*>(orow + 16 * mb) = st.acc_o[mb][nb];
+      if (wave4 == 0 && g == 0) {
+        a.ws_ml[base * 2 + 0] = st.m_run[nb];
+        a.ws_ml[base * 2 + 1] = st.l_run[nb];
       }
     }
   }
 }
 
-// Merge split partials: o = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)).
-__global__ void __launch_bounds__(128) sfa_combine(SfaArgs a) {
-  const int t = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+// Merge split partials: o = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)),
+// M = max(m_s, sink).  One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64),
+// the wave reduces them with shuffles, then each lane accumulates 8 value dims over the splits.
+__global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int th = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
+  const int t = th / a.Hq, h = th % a.Hq;
   const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-  float M = sk;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.ws_ml[(((long)t * a.n_split + s) * a.Hq + h) * 2]);
-  float num[4] = {0.f, 0.f, 0.f, 0.f};
-  float den = (sk == -INFINITY) ? 0.f : exp2f(sk - M);
-  const int d = threadIdx.x * 4;
-  for (int s = 0; s < a.n_split; ++s) {
-    const long base = ((long)t * a.n_split + s) * a.Hq + h;
-    const float ms = a.ws_ml[base * 2];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - M);
-    den += f * a.ws_ml[base * 2 + 1];
-    const v4f o = *reinterpret_cast<const v4f*>(a.ws_o + base * kDv + d);
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < a.n_split) {
+    const long base = ((long)t * a.n_split + lane) * a.Hq + h;
+    ms = a.ws_ml[base * 2];
+    ls = a.ws_ml[base * 2 + 1];
+  }
+  float M = ms;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) num[i] += f * o[i];
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  M = fmaxf(M, sk);
+  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+  float den = f * ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
+  den += (sk == -INFINITY) ? 0.f : exp2f(sk - M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
+  const long sstride = (long)a.Hq * kDv;
+#pragma unroll 8
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float fs = __shfl(f, sp, kWave);
+    const v4f o0 = *reinterpret_cast<const v4f*>(src + sp * sstride);
+    const v4f o1 = *reinterpret_cast<const v4f*>(src + sp * sstride + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { acc[i] += fs * o0[i]; acc[4 + i] += fs * o1[i]; }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint2 pk;
-  pk.x = (uint32_t)f32_to_bf16(num[0] * inv) | ((uint32_t)f32_to_bf16(num[1] * inv) << 16);
-  pk.y = (uint32_t)f32_to_bf16(num[2] * inv) | ((uint32_t)f32_to_bf16(num[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(a.out + ((long)t * a.Hq + h) * kDv + d) = pk;
+  uint4 pk;
+  pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+  pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+  pk.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
+  pk.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
+  *reinterpret_cast<uint4*>(a.out + ((long)t * a.Hq + h) * kDv + lane * 8) = pk;
 }
 
-struct SfaPlan { int nb, n_hg, n_split, kps; };
+struct SfaPlan { int n_hg, n_split, kps; };
 
+// One workgroup per CU (the LDS ring takes ~150 KiB): aim for 256 workgroups.
 static SfaPlan plan(int T, int Hq, int k) {
   SfaPlan p{};
-  p.nb = (Hq % 32 == 0) ? 2 : 1;
-  p.n_hg = Hq / (16 * p.nb);
+  p.n_hg = (Hq + 31) / 32;
   const long base = (long)T * p.n_hg;
   const int max_split = (k + kKT - 1) / kKT;
-  long ns = (512 + base - 1) / base;
+  long ns = (256 + base - 1) / base;
   if (ns < 1) ns = 1;
   if (ns > max_split) ns = max_split;
+  if (ns > 64) ns = 64;                                // the combine reads splits lane-wise
   int kps = (int)((k + ns - 1) / ns);
   kps = (kps + kKT - 1) / kKT * kKT;
   p.kps = kps;
@@ -307,6 +411,8 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
   const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
   if (need && (!ws || ws_bytes < need)) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
   if (need && ((uintptr_t)ws & 255)) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  if ((double)bt->max_kv_len * (double)kv_row_stride * 2.0 >= 4294967296.0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: a sequence's latent rows must span < 4 GiB", fn);
   const long nwg = (long)bt->num_q * p.n_hg * p.n_split;
   if (nwg > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
 
@@ -323,12 +429,10 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)nwg);
   if (p.n_split == 1) {
-    if (p.nb == 2) hipLaunchKernelGGL((dsa::sfa_kernel<2, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dsa::sfa_kernel<1, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((dsa::sfa_kernel<true>), grid, dim3(512), 0, s, a);
   } else {
-    if (p.nb == 2) hipLaunchKernelGGL((dsa::sfa_kernel<2, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dsa::sfa_kernel<1, false>), grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(dsa::sfa_combine, dim3((unsigned)(bt->num_q * Hq)), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((dsa::sfa_kernel<false>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(dsa::sfa_combine, dim3((unsigned)((bt->num_q * Hq + 3) / 4)), dim3(256), 0, s, a);
   }
   return dsa_host::check_launch(fn);
 }

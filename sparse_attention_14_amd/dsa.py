@@ -174,8 +174,9 @@ def dsa_sparse_attn_workspace_size(num_q: int, Hq: int, k: int) -> int:
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    # torch's caching allocator returns blocks aligned to at least 512 bytes
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    # torch's caching allocator returns blocks aligned to at least 512 bytes; zero-filled
+    # because the top-k workspace must start (and is left) zeroed
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def dsa_topk(batch: Batch, scores: torch.Tensor, k: int, idx: Optional[torch.Tensor] = None,

@@ -52,7 +52,7 @@ class StepBuffers:
             scores=torch.empty((T, _scores_ld(batch.max_kv_len)), dtype=torch.float32, device=device),
             idx=torch.empty((T, cfg.k), dtype=torch.int32, device=device),
             out=torch.empty((T, Hq, 512), dtype=torch.bfloat16, device=device),
-            ws_topk=torch.empty(max(1, dsa_topk_workspace_size(T, batch.max_kv_len, cfg.k)),
+            ws_topk=torch.zeros(max(1, dsa_topk_workspace_size(T, batch.max_kv_len, cfg.k)),
                                 dtype=torch.uint8, device=device),
             ws_sfa=torch.empty(nws, dtype=torch.uint8, device=device) if nws else None)
 
