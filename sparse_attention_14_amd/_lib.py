@@ -49,6 +49,8 @@ SIGNATURES = {
     "dsa_indexer_dots_i32": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _I64, _P]),
     "dsa_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_topk": (ctypes.c_int, [_BP, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "dsa_indexer_topk": (ctypes.c_int, [_BP, _I32, _I32, ctypes.c_int, ctypes.c_int, _P, _P, _P,
+                                        _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "dsa_sparse_attn_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_sparse_attn_decode": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
                                               ctypes.c_float, _P, _P, _SZ, _P]),

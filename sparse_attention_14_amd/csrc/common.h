@@ -44,6 +44,16 @@ __device__ __forceinline__ u16 f32_to_f16_bits(float f) {
 template <typename T>
 __device__ __forceinline__ void retire(const T& v) { asm volatile("" :: "v"(v)); }
 
+// Order-preserving key of an fp32 score: unsigned comparison of keys equals numeric comparison
+// of the scores (-0.0 is mapped to +0.0 first, so the two compare equal).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int kHistBins = 2048;          // top-k radix histogram: the top 11 bits of the key
+constexpr int kHistShards = 4;           // copies of each row histogram (spread atomic traffic)
+
 // Flat workgroup id remapped so that consecutive logical ids land on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); logical id
 // w = xcd * per_xcd + slot keeps neighbours (which share data) in one L2.

@@ -27,6 +27,7 @@ struct IdxArgs {
   const uint8_t* q_codes; const void* q_scale; const u16* w;
   const uint8_t* k_cache; const void* k_scale;
   float* scores; int32_t* dots; long ld;
+  uint32_t* hist; int hist_k;            // optional top-k digit histogram [T][kHistShards][kHistBins]
   int H; int ngrp; int scale_f16;
 };
 
@@ -292,6 +293,30 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
       float* dst = a.scores + (long)tj * a.ld + chunk0;
       for (int e = threadIdx.x; e < n; e += 256) dst[e] = scl[j][e];
     }
+    if (a.hist) {
+      // The top-k's first radix pass, fused: histogram of the top 11 key bits of this chunk's
+      // scores per token (LDS, reusing the key buffer), non-zero bins added to one of the
+      // token's histogram shards.  Rows with at most hist_k valid keys get no histogram.
+      uint32_t* hl = reinterpret_cast<uint32_t*>(kl);
+      static_assert(G * kHistBins * 4 <= KB, "histogram does not fit the key buffer");
+      for (int i = threadIdx.x; i < G * kHistBins; i += 256) hl[i] = 0u;
+      __syncthreads();
+      for (int j = 0; j < G; ++j) {
+        const int tj = q_lo + j;
+        if (tj >= q_hi) break;
+        const int pj = a.q_pos[tj];
+        if (pj + 1 <= a.hist_k) continue;
+        const int n = min(kCK, pj + 1 - chunk0);
+        for (int e = threadIdx.x; e < n; e += 256) atomicAdd(&hl[j * kHistBins + (order_key(scl[j][e]) >> 21)], 1u);
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < G * kHistBins; i += 256) {
+        const int j = i / kHistBins;
+        const uint32_t c = hl[i];
+        if (c && q_lo + j < q_hi)
+          atomicAdd(&a.hist[((long)(q_lo + j) * kHistShards + blockIdx.x % kHistShards) * kHistBins + (i % kHistBins)], c);
+      }
+    }
   }
 }
 
@@ -332,7 +357,7 @@ dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn) { return check_b
 static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype code, dsa_dtype sdt,
                                  const void* q, const void* qs, const void* w, const void* k,
                                  const void* ks, float* scores, int32_t* dots, bool want_dots,
-                                 long ld, void* stream, const char* fn) {
+                                 long ld, uint32_t* hist, int hist_k, void* stream, const char* fn) {
   dsa_status st = check_batch(bt, fn);
   if (st != DSA_OK) return st;
   if (!((H == 64 && D == 128) || (H == 8 && D == 64)))
@@ -350,6 +375,7 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.q_start = bt->q_start; a.q_pos = bt->q_pos; a.kv_start = bt->kv_start;
   a.q_codes = (const uint8_t*)q; a.q_scale = qs; a.w = (const dsa::u16*)w;
   a.k_cache = (const uint8_t*)k; a.k_scale = ks; a.scores = scores; a.dots = dots; a.ld = ld;
+  a.hist = hist; a.hist_k = hist_k;
   a.H = H; a.scale_f16 = sdt == DSA_F16;
   const int G = bt->max_q_per_seq >= 3 ? 4 : bt->max_q_per_seq;
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
@@ -376,12 +402,22 @@ extern "C" dsa_status dsa_indexer_scores(const dsa_batch* batch, int32_t H, int3
                                          const void* k_cache, const void* k_scale, float* scores,
                                          int64_t ld, void* stream) {
   return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
-                        k_scale, scores, nullptr, false, ld, stream, "dsa_indexer_scores");
+                        k_scale, scores, nullptr, false, ld, nullptr, 0, stream, "dsa_indexer_scores");
+}
+
+// Scores plus the fused first radix pass of the top-k (used by dsa_indexer_topk).
+dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D, dsa_dtype code_dtype,
+                                   dsa_dtype scale_dtype, const void* q_codes, const void* q_scale,
+                                   const void* w, const void* k_cache, const void* k_scale,
+                                   float* scores, int64_t ld, uint32_t* hist, int32_t k,
+                                   void* stream, const char* fn) {
+  return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                        k_scale, scores, nullptr, false, ld, hist, k, stream, fn);
 }
 
 extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
                                            const int8_t* q_codes, const int8_t* k_cache,
                                            int32_t* dots, int64_t ld, void* stream) {
   return indexer_common(batch, H, D, DSA_I8, DSA_F32, q_codes, nullptr, nullptr, k_cache, nullptr,
-                        nullptr, dots, true, ld, stream, "dsa_indexer_dots_i32");
+                        nullptr, dots, true, ld, nullptr, 0, stream, "dsa_indexer_dots_i32");
 }

@@ -197,6 +197,37 @@ def dsa_topk(batch: Batch, scores: torch.Tensor, k: int, idx: Optional[torch.Ten
     return idx
 
 
+def dsa_indexer_topk(batch: Batch, H: int, D: int, code: str, scale_dt: str, q_codes, q_scale,
+                     w, k_cache, k_scale, k: int, scores: Optional[torch.Tensor] = None,
+                     idx: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexer scores then top-k in one call (the top-k's first radix pass fused into the
+    indexer) -> idx int32 [T, k]; `scores` is written as by dsa_indexer_scores."""
+    T = batch.num_q
+    ct, st = _CODE_TORCH[code], _SCALE_TORCH[scale_dt]
+    _need(q_codes, "q_codes", ct, (T, H, D))
+    _need(q_scale, "q_scale", st, (T, H))
+    _need(w, "w", torch.float16, (T, H))
+    _need(k_cache, "k_cache", ct)
+    _need(k_scale, "k_scale", st)
+    if scores is None:
+        scores = torch.empty((T, _scores_ld(batch.max_kv_len)), dtype=torch.float32,
+                             device=q_codes.device)
+    _need(scores, "scores", torch.float32)
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_codes.device)
+    _need(idx, "idx", torch.int32, (T, k))
+    if ws is None:
+        ws = _workspace(dsa_topk_workspace_size(T, batch.max_kv_len, k), q_codes.device)
+    _need(ws, "ws", torch.uint8)
+    b = batch.c()
+    check("dsa_indexer_topk", lib.dsa_indexer_topk(
+        ctypes.byref(b), H, D, _CODE[code], _SCALE[scale_dt], _ptr(q_codes), _ptr(q_scale), _ptr(w),
+        _ptr(k_cache), _ptr(k_scale), _ptr(scores), scores.shape[1] if scores.dim() == 2 else 0,
+        k, _ptr(idx), _ptr(ws), ws.numel(), _stream()))
+    return idx
+
+
 def dsa_sparse_attn_decode(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
                            sink: Optional[torch.Tensor], scale: float,
                            out: Optional[torch.Tensor] = None,

@@ -1,4 +1,4 @@
-"""One DSA decode step through the C ABI: prolog -> indexer scores -> top-k -> sparse attention.
+"""One DSA decode step through the C ABI: prolog -> indexer scores + top-k -> sparse attention.
 
 [DIA] "Deepseek Indexer Attention" (jsqmd.com/news/787325): the decode layer runs the indexer
 prolog, the Lightning Indexer with its TopK and Sparse Flash Attention in that order (the MLA
@@ -12,8 +12,8 @@ from typing import Optional
 
 import torch
 
-from .dsa import (Batch, _scores_ld, dsa_indexer_prolog, dsa_indexer_scores,
-                  dsa_sparse_attn_decode, dsa_sparse_attn_workspace_size, dsa_topk,
+from .dsa import (Batch, _scores_ld, dsa_indexer_prolog, dsa_indexer_topk,
+                  dsa_sparse_attn_decode, dsa_sparse_attn_workspace_size,
                   dsa_topk_workspace_size)
 
 
@@ -72,8 +72,7 @@ def decode_step(batch: Batch, cfg: IndexerCfg, *, q_in, k_in, new_slots, w, k_ca
                        k_cos=k_cos, k_sin=k_sin, k_slot=new_slots, k_cache=k_cache,
                        k_scale=k_scale, rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
                        rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard)
-    dsa_indexer_scores(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
-                       k_cache, k_scale, scores=buf.scores)
-    dsa_topk(batch, buf.scores, cfg.k, idx=buf.idx, ws=buf.ws_topk)
+    dsa_indexer_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
+                     k_cache, k_scale, cfg.k, scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
     return dsa_sparse_attn_decode(batch, q_attn, kv, buf.idx, sink, scale, out=buf.out,
                                   ws=buf.ws_sfa)

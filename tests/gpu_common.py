@@ -75,6 +75,15 @@ class Gpu:
     def topk(self, scores):
         return dsa.dsa_topk(self.batch, scores, self.cfg.k)
 
+    def indexer_topk(self, ws=None):
+        c = self.cfg
+        scores = torch.empty((self.wl.T, dsa._scores_ld(self.batch.max_kv_len)), dtype=torch.float32,
+                             device="cuda")
+        idx = dsa.dsa_indexer_topk(self.batch, c.H, c.D, c.code, c.scale_dt, self.q_codes,
+                                   self.q_scale, self.d["w"], self.k_cache, self.k_scale, c.k,
+                                   scores=scores, ws=ws)
+        return scores, idx
+
     def sfa(self, idx, sink=True):
         d = self.d
         return dsa.dsa_sparse_attn_decode(self.batch, d["q"], d["kv"], idx,
@@ -166,11 +175,18 @@ def run_e2e(wl, token_subset=None, check_dots=False):
     log("  prolog done on GPU")
     oq = oracle_quant(wl)
     check_prolog(g, oq)
-    sc = g.scores()
-    idx = g.topk(sc)
+    # the fused indexer + top-k (decode-step path), twice on one workspace (it must be left
+    # zeroed), and the separate calls: all three selections must be identical
+    ws = torch.zeros(max(1, dsa.dsa_topk_workspace_size(wl.T, g.batch.max_kv_len, g.cfg.k)),
+                     dtype=torch.uint8, device="cuda")
+    sc, idx = g.indexer_topk(ws)
+    _, idx_again = g.indexer_topk(ws)
+    idx_sep = g.topk(g.scores())
     out = g.sfa(idx)
     torch.cuda.synchronize()
     log("  GPU step done")
+    assert torch.equal(idx, idx_again), "fused top-k changed on workspace reuse"
+    assert torch.equal(idx, idx_sep), "fused and separate top-k differ"
     toks = np.arange(wl.T) if token_subset is None else np.asarray(token_subset)
     sp = wl.spec
     os_rows = oracle.indexer_scores(oq["q_codes"][toks], oq["q_scale"][toks], wl.w[toks], oq["k_codes"],

@@ -70,6 +70,9 @@ def test_validation_errors_before_any_device_call():
     # top-k: k out of range, workspace too small
     assert lib.dsa_topk(ctypes.byref(b), P, 65536, 4096, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
     assert lib.dsa_topk(ctypes.byref(b), P, 65536, 2048, P, P, 16, None) == L.DSA_ERR_WORKSPACE
+    # fused indexer + top-k: the top-k checks run first, then the indexer's
+    assert lib.dsa_indexer_topk(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, 2048, P, P, 16, None) == L.DSA_ERR_WORKSPACE
+    assert lib.dsa_indexer_topk(ctypes.byref(b), 32, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, 2048, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
     # sparse attention: unsupported heads, bad stride, missing workspace
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 64, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_UNSUPPORTED
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 500, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_INVALID_ARG
@@ -90,6 +93,7 @@ def test_empty_batches_are_noops_without_device():
     b = _batch(T=0, B=0, mq=0, ml=0)
     assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_topk(ctypes.byref(b), None, 0, 2048, None, None, 0, None) == L.DSA_OK
+    assert lib.dsa_indexer_topk(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, 2048, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, None, None, 576, None, 2048, None, ctypes.c_float(0.04), None, None, 0, None) == L.DSA_OK
     cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_FP8_E4M3, L.DSA_F16)
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 0, None, None, None, None, None, 0, None, None, None, None, None, None, None) == L.DSA_OK
@@ -102,7 +106,12 @@ def test_workspace_sizes():
     assert L.lib.dsa_sparse_attn_workspace_size(8, 128, 2048) > 0
     # a large batch needs no split partials
     assert L.lib.dsa_sparse_attn_workspace_size(4096, 128, 2048) == 0
-    assert L.lib.dsa_topk_workspace_size(8, 65536, 2048) >= 8 * 65536 * 8
+    # top-k: at least the per-row histograms; grows with the batch and the row length;
+    # 256-byte multiples
+    sz = L.lib.dsa_topk_workspace_size
+    assert sz(8, 65536, 2048) >= 8 * 2048 * 4
+    assert sz(16, 65536, 2048) > sz(8, 65536, 2048) and sz(8, 131072, 2048) > sz(8, 65536, 2048)
+    assert sz(8, 65536, 2048) % 256 == 0
 
 
 def test_binding_rejects_cpu_tensors():
