@@ -34,6 +34,7 @@ constexpr int kTileB = kKT * kRowB;                  // 36864 bytes per tile
 constexpr int kPairLoads = 2 * kTileB / 16 / 512;    // 9 DMA loads per thread per tile pair
 constexpr int kNBuf = 4;                             // tiles in the LDS ring
 constexpr int kMaxKps = 2048;                        // keys per split (LDS index stage)
+constexpr int kQLoads = 5;                           // Q DMA loads per thread (40 x 1 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -46,7 +47,7 @@ struct SfaArgs {
   const u16* q; const u16* kv; long kv_stride; const int32_t* idx; int k;
   const float* sink; float scale_log2;
   u16* out; float* ws_o; float* ws_ml;
-  int T, Hq, n_hg, n_split, kps;
+  int T, B, Hq, n_hg, n_split, kps;
 };
 
 __device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
@@ -219,27 +220,55 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const int h0 = hg * NH;
   const int kbeg = split * a.kps;
   const int nkeys = min(a.k, kbeg + a.kps) - kbeg;
-  const long kv0 = a.kv_start[a.q_seq[t]];
   const unsigned ring_base = (unsigned)(uintptr_t)(lds_u8*)ring;
+
+  // Prologue, two memory round trips before the first MFMA:
+  //  1. Q (this workgroup's 32 heads x 1152 B, laid out like a KV tile) is moved into the ring
+  //     slot of tile 2 with coalesced direct-to-LDS loads; the selected indices, the token's
+  //     sequence and -- for up to 64 sequences -- every sequence's first cache row (picked by
+  //     lane, no dependent load) are loaded alongside;
+  //  2. the first tile pair is gathered (below) while Q moves from LDS into registers.
+  {
+    const u16* qbase = a.q + (long)t * a.Hq * kDqk;     // wave-uniform
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int it = 0; it < kQLoads; ++it) {
+      const int j = min(wave + 8 * it, kTileB / 1024 - 1);   // 36 KiB = 36 x 1 KiB, padded to 40
+      const int o = j * 1024 + ln * 16;
+      const int r = o / kRowB;
+      const int c = ((o % kRowB) >> 4) ^ (r & 7);
+      const uint32_t off = (uint32_t)min(h0 + r, a.Hq - 1) * (uint32_t)kRowB + (uint32_t)c * 16u;
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(qbase),
+                   "{m0}"(ring_base + 2 * kTileB + j * 1024));
+    }
+  }
+  const int seq = a.q_seq[t];
+  int32_t iv[kMaxKps / 512];
+#pragma unroll
+  for (int u = 0; u < kMaxKps / 512; ++u) {
+    const int j = tid + 512 * u;
+    iv[u] = j < nkeys ? a.idx[(long)t * a.k + kbeg + j] : 0;
+  }
+  const long kv_lane = a.kv_start[min(lane, a.B - 1)];
+#pragma unroll
+  for (int u = 0; u < kMaxKps / 512; ++u) {
+    const int j = tid + 512 * u;
+    if (j < nkeys) sidx[j] = iv[u];
+  }
+  long kv0;
+  if (a.B <= 64) {
+    kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_lane >> 32), seq) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)kv_lane, seq));
+  } else {
+    kv0 = a.kv_start[seq];
+  }
   // DMA addressing: a wave-uniform base (the sequence's first latent row, SGPRs) plus a
   // 32-bit per-lane byte offset (the host checks that a sequence spans < 4 GiB)
   const u16* kv_seq = a.kv + kv0 * a.kv_stride;
   const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
-
-  for (int j = tid; j < nkeys; j += 512) sidx[j] = a.idx[(long)t * a.k + kbeg + j];
-  v8bf qf[18];
-  {
-    const int hq = h0 + 16 * hb + c16;                 // heads past Hq (Hq = 16) stay zero
-    const u16* qrow = a.q + ((long)t * a.Hq + min(hq, a.Hq - 1)) * kDqk + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
-      if (hq >= a.Hq) qf[ks] = v8bf{};
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < 18; ++ks) retire(qf[ks]);      // Q landed before the DMA stream
-  __syncthreads();                                     // indices visible
+  retire(kv_lane);
+  __syncthreads();                                     // indices and Q (in LDS) visible
 
   SfaState st;
 #pragma unroll
@@ -257,6 +286,8 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
     // (hoisted, they do not fit the register budget and get spilled)
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    // all index reads first (one LDS round trip), then the nine loads back to back
+    uint32_t off[kPairLoads];
 #pragma unroll
     for (int it = 0; it < kPairLoads; ++it) {
       const int J = wave + 8 * it;
@@ -268,12 +299,30 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
       const int c = ((o % kRowB) >> 4) ^ (r & 7);
       const int key = min(tl * kKT + r, nkeys - 1);
       const int ix = max(sidx[key], 0);                // unused slot: any valid row (masked)
-      const uint32_t off = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
-      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(kv_seq),
+      off[it] = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
+    }
+#pragma unroll
+    for (int it = 0; it < kPairLoads; ++it) {
+      const int J = wave + 8 * it;
+      const int half = J >= kTileB / 1024 ? 1 : 0;
+      const int j = J - half * (kTileB / 1024);
+      const int tl = 2 * k + half;
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off[it]), "s"(kv_seq),
                    "{m0}"(ring_base + (tl % kNBuf) * kTileB + j * 1024));
     }
   };
   if (npairs > 0) issue_pair(0);
+  // Q fragments from LDS (rows 16 hb + c16, the MFMA B operand); heads past Hq stay zero
+  v8bf qf[18];
+  {
+    const int r = 16 * hb + c16;
+    const unsigned char* qt = ring + 2 * kTileB;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      qf[ks] = *reinterpret_cast<const v8bf*>(qt + tile_off(r, 4 * ks + g));
+      if (h0 + r >= a.Hq) qf[ks] = v8bf{};
+    }
+  }
   for (int k = 0; k < npairs; ++k) {
     lds_barrier();                                     // pair k-1 fully consumed (ring slots free)
     if (k + 1 < npairs) { issue_pair(k + 1); wait_vm<kPairLoads>(); } else { wait_vm<0>(); }
@@ -319,10 +368,24 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
 // M = max(m_s, sink).  One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64),
 // the wave reduces them with shuffles, then each lane accumulates 8 value dims over the splits.
 __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
+  constexpr int kPre = 8;                              // splits whose partials load up front
   const int lane = threadIdx.x & 63;
   const int th = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
   const int t = th / a.Hq, h = th % a.Hq;
+  const float* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
+  const long sstride = (long)a.Hq * kDv;
+  // one memory round trip: the first kPre splits' partial outputs and every split's (m, l)
+  v4f p0[kPre], p1[kPre];
+#pragma unroll
+  for (int sp = 0; sp < kPre; ++sp) {
+    p0[sp] = v4f{0.f, 0.f, 0.f, 0.f};
+    p1[sp] = p0[sp];
+    if (sp < a.n_split) {
+      p0[sp] = *reinterpret_cast<const v4f*>(src + sp * sstride);
+      p1[sp] = *reinterpret_cast<const v4f*>(src + sp * sstride + 4);
+    }
+  }
   const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
   float ms = -INFINITY, ls = 0.f;
   if (lane < a.n_split) {
@@ -340,10 +403,13 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
   den += (sk == -INFINITY) ? 0.f : exp2f(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const float* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
-  const long sstride = (long)a.Hq * kDv;
-#pragma unroll 8
-  for (int sp = 0; sp < a.n_split; ++sp) {
+#pragma unroll
+  for (int sp = 0; sp < kPre; ++sp) {
+    const float fs = __shfl(f, sp, kWave);             // 0 for splits past n_split
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { acc[i] += fs * p0[sp][i]; acc[4 + i] += fs * p1[sp][i]; }
+  }
+  for (int sp = kPre; sp < a.n_split; ++sp) {
     const float fs = __shfl(f, sp, kWave);
     const v4f o0 = *reinterpret_cast<const v4f*>(src + sp * sstride);
     const v4f o1 = *reinterpret_cast<const v4f*>(src + sp * sstride + 4);
@@ -420,7 +486,7 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
   a.q_seq = bt->q_seq; a.kv_start = bt->kv_start; a.q = (const dsa::u16*)q;
   a.kv = (const dsa::u16*)kv; a.kv_stride = kv_row_stride; a.idx = idx; a.k = k; a.sink = sink;
   a.scale_log2 = scale * dsa::kLog2e; a.out = (dsa::u16*)out;
-  a.T = bt->num_q; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
+  a.T = bt->num_q; a.B = bt->num_seqs; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
     a.ws_o = (float*)ws;
