@@ -155,6 +155,13 @@ def main():
         dsa.dsa_sparse_attn_decode(batch, s.q, s.kv, s.buf.idx, sink, wl.scale, out=s.buf.out,
                                    ws=s.buf.ws_sfa)
 
+    def st_sfa_split(s):
+        dsa.dsa_sparse_attn_split(batch, s.q, s.kv, s.buf.idx, sink, wl.scale, out=s.buf.out,
+                                  ws=s.buf.ws_sfa)
+
+    def st_sfa_merge(s):
+        dsa.dsa_sparse_attn_merge(batch, Hq, k, sink, s.buf.out, s.buf.ws_sfa)
+
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -206,7 +213,7 @@ def main():
 
     # per-stage / per-kernel timing: R launches of one stage per graph replay
     stages = {"prolog": st_prolog, "indexer": st_indexer, "indexer_topk": st_indexer_topk,
-              "sfa": st_sfa}
+              "sfa": st_sfa, "sfa_split": st_sfa_split, "sfa_merge": st_sfa_merge}
     stage_us = {}
     for name, fn in stages.items():
         g = capture(fn)
@@ -226,10 +233,13 @@ def main():
 
     idx_tops = idx_ops / (stage_us["indexer"] * 1e-6) / 1e12
     sfa_gbps = n_sel * 1152 / (stage_us["sfa"] * 1e-6) / 1e9
-    dominant = max(("indexer", "sfa"), key=lambda n: stage_us[n])
-    dom_bytes = b_indexer if dominant == "indexer" else b_sfa
+    # roofline of the dominant kernel: among the single-kernel calls, the longest per launch;
+    # algorithmic bytes per launch (the split stage: gathered rows, q, indices)
+    single = {"indexer": ("dsa::indexer_kernel", b_indexer),
+              "sfa_split": ("dsa::sfa_kernel", n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4)}
+    dominant = max(single, key=lambda n: stage_us[n])
+    kernel_name, dom_bytes = single[dominant]
     dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
-    kernel_name = {"indexer": "dsa::indexer_kernel", "sfa": "dsa::sfa_kernel"}[dominant]
 
     result = {
         "metric": "DSA decode us/step at B=4,64K ctx; indexer int8 TOPS; SFA gathered-KV GB/s",
@@ -255,7 +265,7 @@ def main():
         "indexer_tops_frac": round(idx_tops / (INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS), 4),
         "sfa_gathered_GBps": round(sfa_gbps, 1),
         "sfa_gathered_frac": round(sfa_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(dom_gbps, 1),
+        "roofline": {"kernel": kernel_name, "call": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(stage_us[dominant], 3)},

@@ -203,6 +203,24 @@ dsa_status dsa_sparse_attn_decode(const dsa_batch* batch, int32_t Hq, const void
                                   int32_t k, const float* sink, float scale, void* out,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The two stages of dsa_sparse_attn_decode, for callers that schedule them apart (same
+ * arguments, validation and errors).  [SFA] steps 1-6 run per split of the selection:
+ * dsa_sparse_attn_split writes each split's unnormalised output with its running max and
+ * sum into ws -- or, when the call needs no workspace (dsa_sparse_attn_workspace_size == 0),
+ * finishes steps 7-8 itself and writes out.  dsa_sparse_attn_merge then applies [SFA] steps
+ * 7-8 over the splits (log-sum-exp merge, sink, bf16 store to out); it reads only ws and sink,
+ * and is a no-op when the workspace size is 0.  Running split then merge on one stream gives
+ * exactly the result of dsa_sparse_attn_decode.
+ */
+dsa_status dsa_sparse_attn_split(const dsa_batch* batch, int32_t Hq, const void* q,
+                                 const void* kv, int64_t kv_row_stride, const int32_t* idx,
+                                 int32_t k, const float* sink, float scale, void* out,
+                                 void* ws, size_t ws_bytes, void* stream);
+dsa_status dsa_sparse_attn_merge(const dsa_batch* batch, int32_t Hq, int32_t k,
+                                 const float* sink, void* out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* ---------------------------------------------------------------- misc -------------------- */
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);

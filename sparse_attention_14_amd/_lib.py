@@ -54,6 +54,9 @@ SIGNATURES = {
     "dsa_sparse_attn_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_sparse_attn_decode": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
                                               ctypes.c_float, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_split": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
+                                             ctypes.c_float, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_merge": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "dsa_last_error": (ctypes.c_char_p, []),
     "dsa_version": (ctypes.c_char_p, []),
 }

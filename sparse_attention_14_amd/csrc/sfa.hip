@@ -458,12 +458,11 @@ extern "C" size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int3
   return o + (n * 2 * 4 + 255) / 256 * 256;
 }
 
-extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, const void* q,
-                                             const void* kv, int64_t kv_row_stride,
-                                             const int32_t* idx, int32_t k, const float* sink,
-                                             float scale, void* out, void* ws, size_t ws_bytes,
-                                             void* stream) {
-  const char* fn = "dsa_sparse_attn_decode";
+// Validates a sparse-attention call and fills the kernel arguments (no launch).
+static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, const void* kv,
+                              int64_t kv_row_stride, const int32_t* idx, int32_t k,
+                              const float* sink, float scale, void* out, void* ws, size_t ws_bytes,
+                              const char* fn, dsa::SfaArgs* args, dsa::SfaPlan* plan) {
   dsa_status st = dsa_check_batch(bt, fn);
   if (st != DSA_OK) return st;
   if (Hq != 16 && Hq != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: Hq must be 16 or 128 (got %d)", fn, Hq);
@@ -481,7 +480,6 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
     return fail(DSA_ERR_UNSUPPORTED, "%s: a sequence's latent rows must span < 4 GiB", fn);
   const long nwg = (long)bt->num_q * p.n_hg * p.n_split;
   if (nwg > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
-
   dsa::SfaArgs a{};
   a.q_seq = bt->q_seq; a.kv_start = bt->kv_start; a.q = (const dsa::u16*)q;
   a.kv = (const dsa::u16*)kv; a.kv_stride = kv_row_stride; a.idx = idx; a.k = k; a.sink = sink;
@@ -492,13 +490,63 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
     a.ws_o = (float*)ws;
     a.ws_ml = (float*)((char*)ws + (n * dsa::kDv * 4 + 255) / 256 * 256);
   }
-  hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)nwg);
-  if (p.n_split == 1) {
-    hipLaunchKernelGGL((dsa::sfa_kernel<true>), grid, dim3(512), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((dsa::sfa_kernel<false>), grid, dim3(512), 0, s, a);
-    hipLaunchKernelGGL(dsa::sfa_combine, dim3((unsigned)((bt->num_q * Hq + 3) / 4)), dim3(256), 0, s, a);
-  }
+  *args = a;
+  *plan = p;
+  return DSA_OK;
+}
+
+static void sfa_launch_split(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipStream_t s) {
+  const dim3 grid((unsigned)((long)a.T * p.n_hg * p.n_split));
+  if (p.n_split == 1) hipLaunchKernelGGL((dsa::sfa_kernel<true>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((dsa::sfa_kernel<false>), grid, dim3(512), 0, s, a);
+}
+
+static void sfa_launch_merge(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipStream_t s) {
+  if (p.n_split > 1)
+    hipLaunchKernelGGL(dsa::sfa_combine, dim3((unsigned)((a.T * a.Hq + 3) / 4)), dim3(256), 0, s, a);
+}
+
+extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, const void* q,
+                                             const void* kv, int64_t kv_row_stride,
+                                             const int32_t* idx, int32_t k, const float* sink,
+                                             float scale, void* out, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  const char* fn = "dsa_sparse_attn_decode";
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
+                                    ws_bytes, fn, &a, &p);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_split(a, p, (hipStream_t)stream);
+  sfa_launch_merge(a, p, (hipStream_t)stream);
+  return dsa_host::check_launch(fn);
+}
+
+extern "C" dsa_status dsa_sparse_attn_split(const dsa_batch* bt, int32_t Hq, const void* q,
+                                            const void* kv, int64_t kv_row_stride,
+                                            const int32_t* idx, int32_t k, const float* sink,
+                                            float scale, void* out, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  const char* fn = "dsa_sparse_attn_split";
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
+                                    ws_bytes, fn, &a, &p);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_split(a, p, (hipStream_t)stream);
+  return dsa_host::check_launch(fn);
+}
+
+extern "C" dsa_status dsa_sparse_attn_merge(const dsa_batch* bt, int32_t Hq, int32_t k,
+                                            const float* sink, void* out, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_sparse_attn_merge";
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  // the merge reads no q / kv / idx: any non-NULL aligned value passes their checks
+  const dsa_status st = sfa_prepare(bt, Hq, out, out, dsa::kDqk, (const int32_t*)out, k, sink,
+                                    1.f, out, ws, ws_bytes, fn, &a, &p);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_merge(a, p, (hipStream_t)stream);
   return dsa_host::check_launch(fn);
 }

@@ -233,6 +233,15 @@ def dsa_sparse_attn_decode(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx:
                            out: Optional[torch.Tensor] = None,
                            ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Sparse attention over the selected latent rows -> bf16 [T, Hq, 512]."""
+    Hq, k, out, ws = _sfa_args(batch, q, kv, idx, sink, out, ws)
+    b = batch.c()
+    check("dsa_sparse_attn_decode", lib.dsa_sparse_attn_decode(
+        ctypes.byref(b), Hq, _ptr(q), _ptr(kv), kv.stride(0), _ptr(idx), k, _ptr(sink),
+        ctypes.c_float(scale), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def _sfa_args(batch: Batch, q, kv, idx, sink, out, ws):
     T = batch.num_q
     if q.dim() != 3:
         raise ValueError("q must be [T, Hq, 576]")
@@ -251,10 +260,33 @@ def dsa_sparse_attn_decode(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx:
     need = dsa_sparse_attn_workspace_size(T, Hq, k)
     if ws is None and need:
         ws = _workspace(need, q.device)
+    return Hq, k, out, ws
+
+
+def dsa_sparse_attn_split(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
+                          sink: Optional[torch.Tensor], scale: float,
+                          out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """First stage of dsa_sparse_attn_decode: per-split partials into ws (or, when no
+    workspace is needed, the final output).  Returns (out, ws) for dsa_sparse_attn_merge."""
+    Hq, k, out, ws = _sfa_args(batch, q, kv, idx, sink, out, ws)
     b = batch.c()
-    check("dsa_sparse_attn_decode", lib.dsa_sparse_attn_decode(
+    check("dsa_sparse_attn_split", lib.dsa_sparse_attn_split(
         ctypes.byref(b), Hq, _ptr(q), _ptr(kv), kv.stride(0), _ptr(idx), k, _ptr(sink),
         ctypes.c_float(scale), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return out, ws
+
+
+def dsa_sparse_attn_merge(batch: Batch, Hq: int, k: int, sink: Optional[torch.Tensor],
+                          out: torch.Tensor, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """Second stage: merge the split partials in ws, apply the sink, write bf16 out."""
+    _need(out, "out", torch.bfloat16, (batch.num_q, Hq, D_V))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (Hq,))
+    b = batch.c()
+    check("dsa_sparse_attn_merge", lib.dsa_sparse_attn_merge(
+        ctypes.byref(b), Hq, k, _ptr(sink), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream()))
     return out
 
 

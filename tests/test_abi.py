@@ -78,6 +78,9 @@ def test_validation_errors_before_any_device_call():
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 500, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_INVALID_ARG
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_WORKSPACE
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, P, P, 576, P, 2048, None, ctypes.c_float(-1.0), P, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_attn_split(ctypes.byref(b), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, None, 0, None) == L.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_attn_merge(ctypes.byref(b), 64, 2048, None, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_attn_merge(ctypes.byref(b), 128, 2048, None, P, None, 0, None) == L.DSA_ERR_WORKSPACE
     # prolog: bad D, bad rope range, missing pointers
     cfg = L.DsaPrologCfg(64, 96, 0, 0, 0, 0, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, None, None, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_UNSUPPORTED

@@ -147,6 +147,23 @@ def test_sparse_attention_isolated(rng, Hq, T, sink, pad):
         assert not out[1].float().abs().sum().item()
 
 
+@pytest.mark.parametrize("Hq,T", [(128, 8), (16, 3), (128, 600)])
+def test_sparse_attention_split_then_merge_equals_decode(rng, Hq, T):
+    """The two stage entry points, run back to back, reproduce the one-call result bit for bit
+    (with split partials for small T, and the direct path when one split suffices)."""
+    lens = list(rng.integers(2500, 5000, size=T))
+    sp = Spec(f"sfa_stages_{Hq}_{T}", 7350 + T, lens, [1] * T, H=8, D=64, k=2048, Hq=Hq)
+    wl = make(sp)
+    idx = torch.from_numpy(workloads.random_topk_idx(rng, wl.q_pos, 2048, pad_frac=0.1)).cuda()
+    d = workloads.device_arrays(wl)
+    batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start)
+    log(f"case sfa split+merge Hq={Hq} T={T} ws={dsa.dsa_sparse_attn_workspace_size(T, Hq, 2048)}")
+    ref = dsa.dsa_sparse_attn_decode(batch, d["q"], d["kv"], idx, d["sink"], wl.scale)
+    out, ws = dsa.dsa_sparse_attn_split(batch, d["q"], d["kv"], idx, d["sink"], wl.scale)
+    dsa.dsa_sparse_attn_merge(batch, Hq, 2048, d["sink"], out, ws)
+    assert torch.equal(out, ref)
+
+
 def test_sparse_attention_strided_kv(rng):
     """kv rows with a stride larger than 576 (e.g. a wider cache row)."""
     sp = Spec("sfa_stride", 7400, [3000, 2500], [1, 1], H=8, D=64, k=1000, Hq=128)
