@@ -44,6 +44,16 @@ __device__ __forceinline__ u16 f32_to_f16_bits(float f) {
 template <typename T>
 __device__ __forceinline__ void retire(const T& v) { asm volatile("" :: "v"(v)); }
 
+// A pointer that is the same in every lane, moved to scalar registers (the direct-to-LDS loads
+// take their base address from SGPRs).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Order-preserving key of an fp32 score: unsigned comparison of keys equals numeric comparison
 // of the scores (-0.0 is mapped to +0.0 first, so the two compare equal).
 __device__ __forceinline__ uint32_t order_key(float f) {

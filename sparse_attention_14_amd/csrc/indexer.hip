@@ -28,7 +28,7 @@ struct IdxArgs {
   const uint8_t* k_cache; const void* k_scale;
   float* scores; int32_t* dots; long ld;
   uint32_t* hist; int hist_k;            // optional top-k digit histogram [T][kHistShards][kHistBins]
-  int H; int ngrp; int scale_f16;
+  int H; int ngrp; int scale_f16; int B; int T;
 };
 
 constexpr int kCK = 512;     // keys per workgroup
@@ -130,52 +130,87 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hv = lane >> 5, col = lane & 31;
   const int b = blockIdx.y / a.ngrp, g = blockIdx.y % a.ngrp;
-  const int q_lo = a.q_start[b] + g * G, q_hi = a.q_start[b + 1];
-  if (q_lo >= q_hi) return;
-  int maxp = -1;
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-    if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
   const int chunk0 = blockIdx.x * kCK;
-  if (chunk0 > maxp) return;
   const int ti = wave % G;                   // this wave's token
+  const int phase = wave / G;
+  // Batch metadata.  Small batches (B < 64, T <= 64) load q_start, q_pos and kv_start as
+  // lane vectors in one memory round trip and pick entries by lane; larger ones chain loads.
+  int q_lo, q_hi, maxp = -1, p;
+  long kv0;
+  if (a.B < 64 && a.T <= 64) {
+    const int qs_l = a.q_start[min(lane, a.B)];
+    const int qp_l = a.q_pos[min(lane, a.T - 1)];
+    const long kv_l = a.kv_start[min(lane, a.B - 1)];
+    q_lo = __builtin_amdgcn_readlane(qs_l, b) + g * G;
+    q_hi = __builtin_amdgcn_readlane(qs_l, b + 1);
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (q_lo + j < q_hi) maxp = max(maxp, __builtin_amdgcn_readlane(qp_l, q_lo + j));
+    const int tt = min(q_lo + ti, a.T - 1);
+    p = q_lo + ti < q_hi ? __builtin_amdgcn_readlane(qp_l, tt) : -1;
+    kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_l >> 32), b) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)kv_l, b));
+  } else {
+    q_lo = a.q_start[b] + g * G;
+    q_hi = a.q_start[b + 1];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
+    p = q_lo + ti < q_hi ? a.q_pos[q_lo + ti] : -1;
+    kv0 = a.kv_start[b];
+  }
+  if (q_lo >= q_hi) return;
+  if (chunk0 > maxp) return;
   const int t = q_lo + ti;
   const bool live = t < q_hi;
-  const int phase = wave / G;
-  const int p = live ? a.q_pos[t] : -1;
-  const long kv0 = a.kv_start[b];
   const int H = a.H;
 
   // Loads below are unconditional (clamped indices, results selected afterwards): a load
   // behind a per-element branch is issued and waited for one at a time.
   const int tc = live ? t : q_hi - 1;
-  KFrag<FP8, D> qf[NMB];
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
-    const int h = min(32 * mb + col, H - 1);
-    load_row_half<FP8, D>(qf[mb], a.q_codes + ((long)tc * H + h) * D + hv * (D / 2));
-  }
-  // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane
+  const int nvalid = min(G, q_hi - q_lo);                // query tokens of this group
+  constexpr int HT = D == 128 ? 64 : 8;                  // indexer heads of the compiled shape
+  constexpr int QB = G * HT * D;                         // the group's query codes (bytes)
+  constexpr int GB = kCK / kGroups * D;                  // one key group in LDS (bytes)
+  constexpr int QG = QB <= GB ? 1 : QB / GB;             // key groups whose LDS holds Q first
+  constexpr int QI = (QB + 4095) / 4096;                 // Q loads per wave (1 KiB each)
+  constexpr int QJ = QB >= 1024 ? QB / 1024 : 1;         // Q loads in all
+  // key group 0 travels with Q; groups 1.. are issued once Q sits in VGPRs (the last QG of
+  // them overwrite Q's LDS) and land while the earlier groups are being consumed
+  constexpr int EARLY = 1;
+  static_assert(EARLY + QG <= kGroups, "Q staging overlaps the first key group");
+  static_assert(QB <= QG * GB && QB % 1024 == 0 || QB < 1024, "Q staging does not fit");
+  // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane:
+  // rows 8 j + 4 hv + e (e < 4) of the block are four consecutive heads, one 8-byte load of w
+  // and one 8- or 16-byte load of q_scale each
   float wq[NMB][16];
   if constexpr (!DOTS) {
+    uint2 wv[NMB][4];
+    uint4 sv[NMB][4];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = 32 * mb + 8 * (i >> 2) + 4 * hv + (i & 3);
-        const long o = (long)tc * H + min(h, H - 1);
-        const float qs = SF16 ? f16_bits_to_f32(((const u16*)a.q_scale)[o]) : ((const float*)a.q_scale)[o];
-        const float v = f16_bits_to_f32(a.w[o]) * qs;
-        wq[mb][i] = (h < H) ? v : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const long o = (long)tc * H + min(32 * mb + 8 * j + 4 * hv, H - 4);
+        wv[mb][j] = *reinterpret_cast<const uint2*>(a.w + o);
+        if (SF16) { const uint2 x = *reinterpret_cast<const uint2*>((const u16*)a.q_scale + o); sv[mb][j] = uint4{x.x, x.y, 0u, 0u}; }
+        else sv[mb][j] = *reinterpret_cast<const uint4*>((const float*)a.q_scale + o);
       }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 32 * mb + 8 * j + 4 * hv + e;
+          const uint32_t ww = e < 2 ? wv[mb][j].x : wv[mb][j].y;
+          const float wf = f16_bits_to_f32((u16)(ww >> (16 * (e & 1))));
+          float qs;
+          if (SF16) { const uint32_t x = e < 2 ? sv[mb][j].x : sv[mb][j].y; qs = f16_bits_to_f32((u16)(x >> (16 * (e & 1)))); }
+          else qs = __uint_as_float(e == 0 ? sv[mb][j].x : e == 1 ? sv[mb][j].y : e == 2 ? sv[mb][j].z : sv[mb][j].w);
+          wq[mb][4 * j + e] = h < H ? wf * qs : 0.f;
+        }
   }
-  // query rows past H are zero (they pair with zero weights; their dots are not stored)
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-    if (32 * mb + col >= H) {
-#pragma unroll
-      for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[mb].v[j] = {};
-    }
   // key scales of this lane's key in each block the wave will visit (row-clamped)
   const int last_row = maxp - chunk0;        // rows past it are clamped (never stored)
   constexpr int NBW = kCK / kBlk / NPH;      // blocks per wave
@@ -188,7 +223,60 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
       ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
     }
   }
-  // retire every load above before the DMA stream starts
+
+  // ---- DMA: the group's query codes (coalesced, rows of D bytes, swizzled like the key rows)
+  // into the LDS of the last QG key groups, then key group 0.  Q moves on to VGPRs before the
+  // remaining key groups are issued.
+  const unsigned kl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kl;
+  const uint8_t* kchunk = uniform_ptr(a.k_cache + (kv0 + chunk0) * D);   // DMA base (SGPRs)
+  {
+    const uint8_t* qbase = uniform_ptr(a.q_codes + (long)q_lo * H * D);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int it = 0; it < QI; ++it) {
+      const int j = min(wave + 4 * it, QJ - 1);
+      const int o = j * 1024 + ln * 16;
+      const int r = o / D;                                 // token * HT + head
+      const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
+      const int tok = min(r / HT, nvalid - 1);
+      dma16(qbase, (uint32_t)((tok * HT + r % HT) * D + c * 16), kl_base + (kGroups - QG) * GB + j * 1024);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < EARLY * PER_GROUP; ++it) {
+    const int j = wave + 4 * it;
+    const int o = j * 1024 + lane * 16;
+    const int r = o / D;
+    const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
+    const int rr = min(r, last_row);
+    dma16(kchunk, (uint32_t)(rr * D + c * 16), kl_base + j * 1024);
+  }
+  idx_wait_vm<EARLY * PER_GROUP>();                      // Q landed (for this wave)
+  idx_lds_barrier();                                     // ... and for every wave
+  KFrag<FP8, D> qf[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int r = ti * HT + min(32 * mb + col, H - 1);
+    const unsigned char* qrow = kl + (kGroups - QG) * GB + r * D;
+#pragma unroll
+    for (int q = 0; q < CPR / 2; ++q) {
+      const int cc = hv * (CPR / 2) + q;
+      const v4i w = *reinterpret_cast<const v4i*>(qrow + ((cc ^ (r & (CPR - 1))) << 4));
+      if constexpr (!FP8) {
+        qf[mb].v[q] = w;
+      } else {
+        qf[mb].v[2 * q] = fp8x8_to_bf16<D>(w[0], w[1]);
+        qf[mb].v[2 * q + 1] = fp8x8_to_bf16<D>(w[2], w[3]);
+      }
+    }
+    if (32 * mb + col >= H) {                            // rows past H are zero
+#pragma unroll
+      for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[mb].v[j] = {};
+    }
+  }
+  // retire every compiler-visible load (the early key groups land with them), and let every
+  // wave finish reading Q before the last groups overwrite its LDS
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -201,13 +289,9 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) retire(ksr[j]);
   }
-  __syncthreads();
-
-  // ---- DMA of the key rows, group by group
-  const unsigned kl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kl;
-  const uint8_t* kchunk = a.k_cache + (kv0 + chunk0) * D;   // wave-uniform DMA base
+  idx_lds_barrier();
 #pragma unroll
-  for (int it = 0; it < INSTR / 4; ++it) {
+  for (int it = EARLY * PER_GROUP; it < INSTR / 4; ++it) {
     const int j = wave + 4 * it;
     const int o = j * 1024 + lane * 16;
     const int r = o / D;
@@ -376,7 +460,7 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.q_codes = (const uint8_t*)q; a.q_scale = qs; a.w = (const dsa::u16*)w;
   a.k_cache = (const uint8_t*)k; a.k_scale = ks; a.scores = scores; a.dots = dots; a.ld = ld;
   a.hist = hist; a.hist_k = hist_k;
-  a.H = H; a.scale_f16 = sdt == DSA_F16;
+  a.H = H; a.scale_f16 = sdt == DSA_F16; a.B = bt->num_seqs; a.T = bt->num_q;
   const int G = bt->max_q_per_seq >= 3 ? 4 : bt->max_q_per_seq;
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
   const long gy = (long)bt->num_seqs * a.ngrp;

@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   //     lane, no dependent load) are loaded alongside;
   //  2. the first tile pair is gathered (below) while Q moves from LDS into registers.
   {
-    const u16* qbase = a.q + (long)t * a.Hq * kDqk;     // wave-uniform
+    const u16* qbase = uniform_ptr(a.q + (long)t * a.Hq * kDqk);
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   }
   // DMA addressing: a wave-uniform base (the sequence's first latent row, SGPRs) plus a
   // 32-bit per-lane byte offset (the host checks that a sequence spans < 4 GiB)
-  const u16* kv_seq = a.kv + kv0 * a.kv_stride;
+  const u16* kv_seq = uniform_ptr(a.kv + kv0 * a.kv_stride);
   const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
   retire(kv_lane);
   __syncthreads();                                     // indices and Q (in LDS) visible
