@@ -206,8 +206,8 @@ dsa_status dsa_sparse_attn_decode(const dsa_batch* batch, int32_t Hq, const void
 /*
  * The two stages of dsa_sparse_attn_decode, for callers that schedule them apart (same
  * arguments, validation and errors).  [SFA] steps 1-6 run per split of the selection:
- * dsa_sparse_attn_split writes each split's unnormalised output with its running max and
- * sum into ws -- or, when the call needs no workspace (dsa_sparse_attn_workspace_size == 0),
+ * dsa_sparse_attn_split writes each split's softmax-weighted average (bf16) with its running
+ * max and sum (fp32) into ws -- or, when the call needs no workspace (dsa_sparse_attn_workspace_size == 0),
  * finishes steps 7-8 itself and writes out.  dsa_sparse_attn_merge then applies [SFA] steps
  * 7-8 over the splits (log-sum-exp merge, sink, bf16 store to out); it reads only ws and sink,
  * and is a no-op when the workspace size is 0.  Running split then merge on one stream gives

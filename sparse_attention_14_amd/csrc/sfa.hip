@@ -20,8 +20,9 @@
 //   PV     : O^T = V^T . P^T; wave w owns value dims 128w..128w+127 for all NH heads, so the
 //            accumulator of head h lives in the lanes with lane%16 == h%16 and the softmax
 //            rescale is per lane
-// A split writes (unnormalised O, running max, running sum) when the selection is spread over
-// several workgroups; the combine kernel merges them with the sink.  With one split the main
+// A split writes its own softmax average O / l in bf16 with its running max and sum (fp32)
+// when the selection is spread over several workgroups; the combine kernel merges them in fp32
+// with the sink.  With one split the main
 // kernel applies the sink and writes bf16 directly.
 #include "common.h"
 
@@ -46,7 +47,7 @@ struct SfaArgs {
   const int32_t* q_seq; const int64_t* kv_start;
   const u16* q; const u16* kv; long kv_stride; const int32_t* idx; int k;
   const float* sink; float scale_log2;
-  u16* out; float* ws_o; float* ws_ml;
+  u16* out; u16* ws_o; float* ws_ml;
   int T, B, Hq, n_hg, n_split, kps;
 };
 
@@ -352,10 +353,18 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
         *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
       }
     } else {
+      // the split's own softmax average O / l (a convex combination of value rows) in bf16;
+      // the merge weighs it by 2^(m - M) l in fp32
       const long base = ((long)t * a.n_split + split) * a.Hq + h;
-      float* orow = a.ws_o + base * kDv + 64 * wave4 + 4 * g;
+      const float inv = st.l_run[nb] > 0.f ? 1.f / st.l_run[nb] : 0.f;
+      u16* orow = a.ws_o + base * kDv + 64 * wave4 + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) *reinterpret_cast<v4f*>(orow + 16 * mb) = st.acc_o[mb][nb];
+      for (int mb = 0; mb < 4; ++mb) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][0] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][2] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
+      }
       if (wave4 == 0 && g == 0) {
         a.ws_ml[base * 2 + 0] = st.m_run[nb];
         a.ws_ml[base * 2 + 1] = st.l_run[nb];
@@ -364,27 +373,24 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   }
 }
 
-// Merge split partials: o = sum_s 2^(m_s - M) O_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)),
-// M = max(m_s, sink).  One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64),
-// the wave reduces them with shuffles, then each lane accumulates 8 value dims over the splits.
+// Merge split partials: with a_s = O_s / l_s (stored bf16), m_s, l_s (fp32) per split,
+//   o = sum_s 2^(m_s - M) l_s a_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)),  M = max(m_s, sink).
+// One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64), the wave reduces
+// them with shuffles, then each lane accumulates 8 value dims over the splits.
 __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   constexpr int kPre = 8;                              // splits whose partials load up front
   const int lane = threadIdx.x & 63;
   const int th = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
   const int t = th / a.Hq, h = th % a.Hq;
-  const float* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
+  const u16* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
   const long sstride = (long)a.Hq * kDv;
   // one memory round trip: the first kPre splits' partial outputs and every split's (m, l)
-  v4f p0[kPre], p1[kPre];
+  uint4 pv[kPre];
 #pragma unroll
   for (int sp = 0; sp < kPre; ++sp) {
-    p0[sp] = v4f{0.f, 0.f, 0.f, 0.f};
-    p1[sp] = p0[sp];
-    if (sp < a.n_split) {
-      p0[sp] = *reinterpret_cast<const v4f*>(src + sp * sstride);
-      p1[sp] = *reinterpret_cast<const v4f*>(src + sp * sstride + 4);
-    }
+    pv[sp] = uint4{0u, 0u, 0u, 0u};
+    if (sp < a.n_split) pv[sp] = *reinterpret_cast<const uint4*>(src + sp * sstride);
   }
   const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
   float ms = -INFINITY, ls = 0.f;
@@ -397,25 +403,24 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
   M = fmaxf(M, sk);
-  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-  float den = f * ls;
+  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M) * ls;   // split weight
+  float den = f;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
   den += (sk == -INFINITY) ? 0.f : exp2f(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float fs, const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int sp = 0; sp < kPre; ++sp) {
-    const float fs = __shfl(f, sp, kWave);             // 0 for splits past n_split
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += fs * bf16_to_f32((u16)w[i]);
+      acc[2 * i + 1] += fs * bf16_to_f32((u16)(w[i] >> 16));
+    }
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { acc[i] += fs * p0[sp][i]; acc[4 + i] += fs * p1[sp][i]; }
-  }
-  for (int sp = kPre; sp < a.n_split; ++sp) {
-    const float fs = __shfl(f, sp, kWave);
-    const v4f o0 = *reinterpret_cast<const v4f*>(src + sp * sstride);
-    const v4f o1 = *reinterpret_cast<const v4f*>(src + sp * sstride + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { acc[i] += fs * o0[i]; acc[4 + i] += fs * o1[i]; }
-  }
+  for (int sp = 0; sp < kPre; ++sp) add(__shfl(f, sp, kWave), pv[sp]);   // 0 past n_split
+  for (int sp = kPre; sp < a.n_split; ++sp)
+    add(__shfl(f, sp, kWave), *reinterpret_cast<const uint4*>(src + sp * sstride));
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint4 pk;
   pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
@@ -454,7 +459,7 @@ extern "C" size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int3
   const dsa::SfaPlan p = dsa::plan(num_q, Hq, k);
   if (p.n_split <= 1) return 0;
   const size_t n = (size_t)num_q * p.n_split * Hq;
-  const size_t o = (n * dsa::kDv * 4 + 255) / 256 * 256;
+  const size_t o = (n * dsa::kDv * 2 + 255) / 256 * 256;
   return o + (n * 2 * 4 + 255) / 256 * 256;
 }
 
@@ -487,8 +492,8 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   a.T = bt->num_q; a.B = bt->num_seqs; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
-    a.ws_o = (float*)ws;
-    a.ws_ml = (float*)((char*)ws + (n * dsa::kDv * 4 + 255) / 256 * 256);
+    a.ws_o = (dsa::u16*)ws;
+    a.ws_ml = (float*)((char*)ws + (n * dsa::kDv * 2 + 255) / 256 * 256);
   }
   *args = a;
   *plan = p;
