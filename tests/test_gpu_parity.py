@@ -28,6 +28,9 @@ SMALL = {
                                   rope_interleaved=True, k=300, Hq=16),
     "no_sink": Spec("small_no_sink", 7006, [2500], [1], k=2048, Hq=128, sink=False),
     "many_tokens": Spec("small_many_tokens", 7005, [4096, 4096], [128, 128], k=256, Hq=128),
+    # more than 64 sequences: the kernels' per-lane batch-metadata path does not apply
+    "many_seqs": Spec("small_many_seqs", 7007, [300 + 37 * i for i in range(80)], [1] * 80, H=8,
+                      D=64, scale_dt="f32", k=256, Hq=16),
 }
 
 
