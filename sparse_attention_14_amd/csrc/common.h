@@ -29,6 +29,12 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<u16>(u >> 16);
 }
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // fp16 <-> fp32 (IEEE binary16; narrowing rounds to nearest even).
 __device__ __forceinline__ float f16_bits_to_f32(u16 h) {

@@ -10,20 +10,20 @@
 // on-chip buffer -- here the selected rows are gathered straight into LDS.
 //
 // Decomposition.  The latent KV is one head shared by all query heads (MLA absorbed), so a
-// workgroup handles one query token, NH = 16*NB query heads and a contiguous range (split)
-// of its selected keys, in tiles of 64 keys:
-//   gather : 64 rows x 1152 B into LDS (row pitch 1168 B: 16-B reads of 8 consecutive rows
-//            hit distinct banks)
-//   QK^T   : S^T = K . Q^T on v_mfma_f32_16x16x32_bf16; wave w owns keys 16w..16w+15 of the
-//            tile, Q (NH heads x 576) stays in VGPRs as the B operand for the whole split
-//   softmax: per-head tile max via LDS, exp2 in the log2 domain, P in bf16 through LDS
-//   PV     : O^T = V^T . P^T; wave w owns value dims 128w..128w+127 for all NH heads, so the
-//            accumulator of head h lives in the lanes with lane%16 == h%16 and the softmax
-//            rescale is per lane
+// workgroup (8 waves) handles one query token, 32 query heads and a contiguous range (split)
+// of its selected keys, in tiles of 32 keys:
+//   gather : 32 rows x 1152 B straight into LDS by two loader waves; a 4-slot ring (144 KiB)
+//            holds the tile being scored, the tile being multiplied with V and two in flight
+//   QK^T   : S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 by two score waves (16 heads each, all 32
+//            keys and 576 dims); Q stays in VGPRs as the B operand
+//   softmax: inside the score wave (tile max across lanes with the gfx950 row swaps), exp2 in
+//            the log2 domain, P in bf16 through LDS
+//   PV     : O^T = V^T . P^T by four value waves, wave owns value dims 128w..128w+127 for all 32
+//            heads, one tile behind the score waves, so the accumulator of head h lives in the
+//            lanes with lane%16 == h%16 and the softmax rescale is per lane
 // A split writes its own softmax average O / l in bf16 with its running max and sum (fp32)
 // when the selection is spread over several workgroups; the combine kernel merges them in fp32
-// with the sink.  With one split the main
-// kernel applies the sink and writes bf16 directly.
+// with the sink.  With one split the main kernel applies the sink and writes bf16 directly.
 #include "common.h"
 
 namespace dsa {
@@ -32,7 +32,6 @@ constexpr int kDqk = 576, kDv = 512;
 constexpr int kKT = 32;                              // keys per tile
 constexpr int kRowB = kDqk * 2;                      // 1152 bytes per latent row
 constexpr int kTileB = kKT * kRowB;                  // 36864 bytes per tile
-constexpr int kPairLoads = 2 * kTileB / 16 / 512;    // 9 DMA loads per thread per tile pair
 constexpr int kNBuf = 4;                             // tiles in the LDS ring
 constexpr int kMaxKps = 2048;                        // keys per split (LDS index stage)
 constexpr int kQLoads = 5;                           // Q DMA loads per thread (40 x 1 KiB)
@@ -51,7 +50,6 @@ struct SfaArgs {
   int T, B, Hq, n_hg, n_split, kps;
 };
 
-__device__ __forceinline__ float exp2_or_zero(float x) { return x == -INFINITY ? 0.f : exp2f(x); }
 
 // Rows are stored unpadded (1152 B) with the 16-byte chunk c of row r at chunk c ^ (r & 7):
 // 16-byte reads of one logical chunk from 8 consecutive rows then fall in distinct banks.
@@ -73,146 +71,156 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-struct SfaState {
-  v4f acc_o[4][2];             // O^T[64-dim slice of this wave][32 heads]
-  float m_run[2], l_run[2];    // per head 16 nb + c16 (identical in every wave)
-};
+// Reductions over the four 16-lane rows of a wave (lane l with l ^ 16, l ^ 32, l ^ 48) on the
+// gfx950 row-swap instructions: two VALU steps instead of two LDS-path shuffles.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 constexpr float kLazy = 8.f;   // log2-domain headroom before the running max is moved
-constexpr int kPP = 2 * kKT * 2 + 16;   // P row pitch: 64 keys (a tile pair) + 16 B pad
+constexpr int kPP = kKT * 2 + 16;        // P row pitch: 32 keys (a tile) + 16 B pad
 
-// One tile pair (64 keys) on 8 waves.
-//  S^T = K Q^T : wave w takes tile 2k + (w>>2), keys 16 (w&1) .. +15, heads 16 ((w>>1)&1) .. +15
-//                (Q of its 16 heads stays in VGPRs as the MFMA B operand).
-//  softmax     : per-head pair max through LDS; the reference max m only moves when the pair's
-//                max exceeds it by more than kLazy, so P < 2^kLazy and the accumulators are
-//                rarely rescaled (the final normalisation uses the same m: exact).
-//  O^T += V^T P^T : wave w owns value dims 64 w .. +63 for all 32 heads over both tiles
-//                (V^T via ds_read_b64_tr_b16, P^T from LDS).
-__device__ __forceinline__ void pair_step(SfaState& st, const unsigned char* t0,
-                                          const unsigned char* t1, const v8bf* qf,
-                                          const int* sidx, int key0, int nkeys, float scale_log2,
-                                          unsigned char* pt, float (*red_max)[32],
-                                          float (*red_sum)[32]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// The workgroup's eight waves take three roles and work one tile apart:
+//  * score waves 0-1, wave = head half hb: S^T = K Q^T for all 32 keys of tile k and heads
+//    16 hb .. +15 over all 576 dims (two key blocks x eighteen v_mfma_f32_16x16x32_bf16 steps;
+//    Q of the 16 heads stays in VGPRs as the B operand), then the online softmax of tile k inside
+//    the wave: tile max, P = 2^(z - m) in bf16 and the rescale factor of the accumulators;
+//  * loader waves 2-3: the gather of the tiles into the LDS ring;
+//  * value waves 4-7, wave = value dims 128 (w - 4) .. +127 for all 32 heads: O^T += V^T P^T for
+//    tile k - 1 (V^T through ds_read_b64_tr_b16, P^T from LDS).
+// Step k has one barrier (tile k landed; P and the rescale factors of tile k - 1 published).  P
+// and the factors are double buffered, so the score waves may publish tile k while the value
+// waves still read tile k - 1.  The reference max m only moves when the tile's max exceeds it by
+// more than kLazy, so P < 2^kLazy and the accumulators are rarely rescaled (the final
+// normalisation uses the same m: exact).
+
+// Score wave, tile k: masked S^T blocks in the log2 domain and the softmax of tile k for heads
+// 16 hb .. +15.  Publishes P (bf16) and the rescale factor; updates the running max and sum.
+__device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf* qf, const int* sidx,
+                                           int key0, int nkeys, float scale_log2, float& m_run,
+                                           float& l_run, unsigned char* pt, float* alpha_out) {
+  const int lane = threadIdx.x & 63, hb = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int th = wave >> 2, kh = wave & 1, hb = (wave >> 1) & 1;
-  const int q4 = 2 * th + kh;                          // key quarter of the pair
-  const unsigned char* tile = th ? t1 : t0;
-  v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-  {
-    const int r = 16 * kh + c16;
-    // K fragments are read two k-steps ahead of their MFMAs; the scheduling barriers keep the
-    // compiler from hoisting all 18 reads to the top.
-    v8bf a0 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, g));
-    v8bf a1 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 + g));
+  // the keys' indices (-1 = unused slot), four per lane in one read; entries past nkeys are
+  // stale but masked by the bound
+  int4 iv[2];
 #pragma unroll
-    for (int ks = 0; ks < 18; ks += 2) {
-      v8bf n0 = a0, n1 = a1;
-      if (ks + 2 < 18) {
-        n0 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 * ks + 8 + g));
-        n1 = *reinterpret_cast<const v8bf*>(tile + tile_off(r, 4 * ks + 12 + g));
-      }
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], s1, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      a0 = n0; a1 = n1;
-    }
+  for (int kb = 0; kb < 2; ++kb) iv[kb] = *reinterpret_cast<const int4*>(sidx + key0 + 16 * kb + 4 * g);
+  // all 36 K fragments are requested before the first MFMA (LDS latency is a few hundred
+  // cycles under load); the scheduling barrier keeps the compiler from interleaving them
+  v8bf k0[18], k1[18];
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    k0[ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(c16, 4 * ks + g));
+    k1[ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(16 + c16, 4 * ks + g));
   }
-  v4f s = s0 + s1;
+  __builtin_amdgcn_sched_barrier(0);
+  // four independent accumulation chains (two per key block): a chain of dependent MFMAs is
+  // bound by their latency, four chains by the matrix core's issue rate
+  v4f sa[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) sa[0][c] = sa[1][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    sa[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[ks], qf[ks], sa[0][ks & 1], 0, 0, 0);
+    sa[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[ks], qf[ks], sa[1][ks & 1], 0, 0, 0);
+  }
+  const v4f s0 = sa[0][0] + sa[0][1], s1 = sa[1][0] + sa[1][1];
+  // unused slots and keys past the split's end carry index -1 (the prologue pads the index
+  // stage to whole tiles)
+  float z[2][4];
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int key = key0 + 16 * q4 + 4 * g + e;
-    const float z = (key < nkeys && sidx[key] >= 0) ? s[e] * scale_log2 : -INFINITY;
-    s[e] = z;
-    m = fmaxf(m, z);
-  }
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  if (g == 0) red_max[q4][16 * hb + c16] = m;
-  lds_barrier();
-  float alpha[2], mnew[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int h = 16 * nb + c16;
-    const float tm = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-    const float mo = st.m_run[nb];
-    const bool move = (mo == -INFINITY) ? (tm != -INFINITY) : (tm > mo + kLazy);
-    mnew[nb] = move ? tm : mo;
-    alpha[nb] = move ? ((mo == -INFINITY) ? 0.f : exp2f(mo - tm)) : 1.f;
-  }
-  {
-    const float mn = mnew[hb];
-    float ps = 0.f;
-    u16 pb[4];
+  for (int kb = 0; kb < 2; ++kb) {
+    const int ix[4] = {iv[kb].x, iv[kb].y, iv[kb].z, iv[kb].w};
+    const v4f sv = kb ? s1 : s0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pv = mn == -INFINITY ? 0.f : exp2_or_zero(s[e] - mn);
-      pb[e] = f32_to_bf16(pv);
-      ps += bf16_to_f32(pb[e]);
+      z[kb][e] = ix[e] >= 0 ? sv[e] * scale_log2 : -INFINITY;
+      m = fmaxf(m, z[kb][e]);
     }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    const int h = 16 * hb + c16;
-    if (g == 0) red_sum[q4][h] = ps;
+  }
+  const float tm = rows_max(m);
+  const bool move = (m_run == -INFINITY) ? (tm != -INFINITY) : (tm > m_run + kLazy);
+  const float mnew = move ? tm : m_run;
+  // v_exp_f32 directly: its arguments are <= kLazy, and -inf gives 0
+  const float alpha = move ? __builtin_amdgcn_exp2f(m_run - tm) : 1.f;   // m_run = -inf: 0
+  const float mref = mnew == -INFINITY ? 0.f : mnew;   // all keys masked so far: every z is -inf
+  float ps = 0.f;
+  const int h = 16 * hb + c16;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
     uint2 pk;
-    pk.x = (uint32_t)pb[0] | ((uint32_t)pb[1] << 16);
-    pk.y = (uint32_t)pb[2] | ((uint32_t)pb[3] << 16);
-    *reinterpret_cast<uint2*>(pt + h * kPP + (16 * q4 + 4 * g) * 2) = pk;
+    pk.x = pack_bf16x2(__builtin_amdgcn_exp2f(z[kb][0] - mref), __builtin_amdgcn_exp2f(z[kb][1] - mref));
+    pk.y = pack_bf16x2(__builtin_amdgcn_exp2f(z[kb][2] - mref), __builtin_amdgcn_exp2f(z[kb][3] - mref));
+    // the sum uses the rounded values the value waves multiply with
+    ps += (__uint_as_float(pk.x << 16) + __uint_as_float(pk.x & 0xFFFF0000u)) +
+          (__uint_as_float(pk.y << 16) + __uint_as_float(pk.y & 0xFFFF0000u));
+    *reinterpret_cast<uint2*>(pt + h * kPP + (16 * kb + 4 * g) * 2) = pk;
   }
-  lds_barrier();
-  bool rescale = false;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int h = 16 * nb + c16;
-    st.l_run[nb] = alpha[nb] * st.l_run[nb] + (red_sum[0][h] + red_sum[1][h]) + (red_sum[2][h] + red_sum[3][h]);
-    st.m_run[nb] = mnew[nb];
-    rescale |= alpha[nb] != 1.f;
-  }
-  if (__any(rescale)) {                                // wave-uniform, rare after the first pair
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) { st.acc_o[mb][0] *= alpha[0]; st.acc_o[mb][1] *= alpha[1]; }
-  }
+  l_run = alpha * l_run + rows_sum(ps);
+  m_run = mnew;
+  if (g == 0) alpha_out[h] = alpha;
+}
+
+// Value wave, tile j: O^T[128 dims][32 heads] += V^T P^T with the rescale of tile j applied first.
+__device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* tile, const unsigned char* pt,
+                                           const float* alpha) {
+  const int lane = threadIdx.x & 63, ow = (threadIdx.x >> 6) - 4;
+  const int g = lane >> 4, c16 = lane & 15;
+  const lds_u8* tl = (const lds_u8*)tile;
   // V^T via ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 values of row
-  // kb + j/4, columns d0 + 4 (j%4) .. +3; lane i receives the 4 rows of column d0 + i.
+  // 8 g + j/4 (+4), columns d0 + 4 (j%4) .. +3; lane i receives the 4 rows of column d0 + i.
+  v4s lo[8], hi[8];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const lds_u8* tl = (const lds_u8*)(tt ? t1 : t0);
-    v8bf pf[2];
+  for (int mb = 0; mb < 8; ++mb) {
+    const int col = 128 * ow + 16 * mb + 4 * (c16 & 3);
+    const int r0 = 8 * g + (c16 >> 2), r1 = r0 + 4;
+    const int c = col >> 3, wi = (col & 7) * 2;
+    lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r0, c) + wi));
+    hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r1, c) + wi));
+  }
+  v8bf pf[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      pf[nb] = *reinterpret_cast<const v8bf*>(pt + (16 * nb + c16) * kPP + (32 * tt + 8 * g) * 2);
+  for (int nb = 0; nb < 2; ++nb)
+    pf[nb] = *reinterpret_cast<const v8bf*>(pt + (16 * nb + c16) * kPP + (8 * g) * 2);
+  const float a0 = alpha[c16], a1 = alpha[16 + c16];
+  if (__any(a0 != 1.f || a1 != 1.f)) {               // wave-uniform, rare after the first tile
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int col = 64 * wave + 16 * mb + 4 * (c16 & 3);
-      const int r0 = 8 * g + (c16 >> 2), r1 = r0 + 4;
-      const int c = col >> 3, wi = (col & 7) * 2;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r0, c) + wi));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r1, c) + wi));
-      const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      st.acc_o[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], st.acc_o[mb][0], 0, 0, 0);
-      st.acc_o[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], st.acc_o[mb][1], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int mb = 0; mb < 8; ++mb) { acc[mb][0] *= a0; acc[mb][1] *= a1; }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[mb][0], lo[mb][1], lo[mb][2], lo[mb][3],
+                                                 hi[mb][0], hi[mb][1], hi[mb][2], hi[mb][3]});
+    acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], acc[mb][0], 0, 0, 0);
+    acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], acc[mb][1], 0, 0, 0);
   }
 }
 
 // One workgroup (8 waves): token t, query heads h0 .. h0+31, selected keys [kbeg, kbeg+nkeys),
-// consumed as pairs of 32-key tiles.  Tiles flow HBM -> 4-slot LDS ring (the next pair in
-// flight while the current pair is consumed) -> MFMA; 8 waves give each SIMD two waves that
-// hide each other's latency.
+// consumed as 32-key tiles through a 4-slot LDS ring: while the score waves work on tile k and
+// the value waves on tile k - 1, tiles k + 1 and k + 2 are in flight.
 template <bool FINAL>
 __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   constexpr int NH = 32;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kNBuf * kTileB];
-  __shared__ __attribute__((aligned(16))) unsigned char pt[NH * kPP];
-  __shared__ float red_max[4][NH];
-  __shared__ float red_sum[4][NH];
-  __shared__ int sidx[kMaxKps];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[2][NH * kPP];
+  __shared__ float abuf[2][NH];
+  __shared__ float fin[2][NH];
+  __shared__ __attribute__((aligned(16))) int sidx[kMaxKps];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15, hb = (wave >> 1) & 1;
+  const int g = lane >> 4, c16 = lane & 15;
   const int nwg = a.T * a.n_hg * a.n_split;
   const int lid = xcd_remap(blockIdx.x, nwg);
   const int hg = lid % a.n_hg;
@@ -224,11 +232,11 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const unsigned ring_base = (unsigned)(uintptr_t)(lds_u8*)ring;
 
   // Prologue, two memory round trips before the first MFMA:
-  //  1. Q (this workgroup's 32 heads x 1152 B, laid out like a KV tile) is moved into the ring
-  //     slot of tile 2 with coalesced direct-to-LDS loads; the selected indices, the token's
-  //     sequence and -- for up to 64 sequences -- every sequence's first cache row (picked by
-  //     lane, no dependent load) are loaded alongside;
-  //  2. the first tile pair is gathered (below) while Q moves from LDS into registers.
+  //  1. Q (this workgroup's 32 heads x 1152 B, laid out like a KV tile) is moved into ring slot
+  //     3 with coalesced direct-to-LDS loads; the selected indices, the token's sequence and --
+  //     for up to 64 sequences -- every sequence's first cache row (picked by lane, no dependent
+  //     load) are loaded alongside;
+  //  2. tiles 0 and 1 are gathered while the score waves move Q from LDS into registers.
   {
     const u16* qbase = uniform_ptr(a.q + (long)t * a.Hq * kDqk);
     int ln = lane;
@@ -241,7 +249,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
       const int c = ((o % kRowB) >> 4) ^ (r & 7);
       const uint32_t off = (uint32_t)min(h0 + r, a.Hq - 1) * (uint32_t)kRowB + (uint32_t)c * 16u;
       asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(qbase),
-                   "{m0}"(ring_base + 2 * kTileB + j * 1024));
+                   "{m0}"(ring_base + 3 * kTileB + j * 1024));
     }
   }
   const int seq = a.q_seq[t];
@@ -252,10 +260,11 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
     iv[u] = j < nkeys ? a.idx[(long)t * a.k + kbeg + j] : 0;
   }
   const long kv_lane = a.kv_start[min(lane, a.B - 1)];
+  const int nkeys_pad = (nkeys + kKT - 1) / kKT * kKT;
 #pragma unroll
   for (int u = 0; u < kMaxKps / 512; ++u) {
     const int j = tid + 512 * u;
-    if (j < nkeys) sidx[j] = iv[u];
+    if (j < nkeys_pad) sidx[j] = j < nkeys ? iv[u] : -1;
   }
   long kv0;
   if (a.B <= 64) {
@@ -269,105 +278,129 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const u16* kv_seq = uniform_ptr(a.kv + kv0 * a.kv_stride);
   const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
   retire(kv_lane);
-  __syncthreads();                                     // indices and Q (in LDS) visible
-
-  SfaState st;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) { st.acc_o[mb][0] = v4f{0.f, 0.f, 0.f, 0.f}; st.acc_o[mb][1] = st.acc_o[mb][0]; }
-  st.m_run[0] = st.m_run[1] = -INFINITY;
-  st.l_run[0] = st.l_run[1] = 0.f;
+  wait_vm<0>();                                        // this wave's Q loads have landed
+  lds_barrier();                                       // indices and Q (in LDS) visible
 
   const int nt = (nkeys + kKT - 1) / kKT;
-  const int npairs = (nt + 1) / 2;
-  // a pair = tiles 2k, 2k+1 in ring slots (2k)%4, (2k+1)%4: 72 wave-instructions of 1 KiB,
-  // J = wave + 8 it (it < 9), so every thread issues exactly kPairLoads DMA loads per pair.
-  // A tile past nt (odd tile count) loads clamped, valid rows whose keys are masked.
-  auto issue_pair = [&](int k) {
-    // opaque lane id: keeps the per-load offsets from being hoisted out of the pair loop
-    // (hoisted, they do not fit the register budget and get spilled)
+  const int role = __builtin_amdgcn_readfirstlane(wave < 2 ? 0 : (wave < 4 ? 1 : 2));  // score, loader, value
+  // Loader wave lw gathers 1-KiB pieces J = lw + 2 it (it < 18) of tile i into ring slot i % 4.
+  // Rows past nkeys load clamped, valid rows whose keys are masked.  The per-lane offsets of the
+  // next tile are read ahead (offs), so a tile's loads issue right after the barrier.
+  uint32_t offs[18];
+  auto tile_offsets = [&](int i) {
+    // opaque lane id: keeps the per-load offsets from being hoisted out of the tile loop
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    // all index reads first (one LDS round trip), then the nine loads back to back
-    uint32_t off[kPairLoads];
 #pragma unroll
-    for (int it = 0; it < kPairLoads; ++it) {
-      const int J = wave + 8 * it;
-      const int half = J >= kTileB / 1024 ? 1 : 0;
-      const int j = J - half * (kTileB / 1024);
-      const int tl = 2 * k + half;
-      const int o = j * 1024 + ln * 16;
+    for (int it = 0; it < 18; ++it) {
+      const int J = (wave - 2) + 2 * it;
+      const int o = J * 1024 + ln * 16;
       const int r = o / kRowB;
       const int c = ((o % kRowB) >> 4) ^ (r & 7);
-      const int key = min(tl * kKT + r, nkeys - 1);
+      const int key = min(i * kKT + r, nkeys - 1);
       const int ix = max(sidx[key], 0);                // unused slot: any valid row (masked)
-      off[it] = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
-    }
-#pragma unroll
-    for (int it = 0; it < kPairLoads; ++it) {
-      const int J = wave + 8 * it;
-      const int half = J >= kTileB / 1024 ? 1 : 0;
-      const int j = J - half * (kTileB / 1024);
-      const int tl = 2 * k + half;
-      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off[it]), "s"(kv_seq),
-                   "{m0}"(ring_base + (tl % kNBuf) * kTileB + j * 1024));
+      offs[it] = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
     }
   };
-  if (npairs > 0) issue_pair(0);
-  // Q fragments from LDS (rows 16 hb + c16, the MFMA B operand); heads past Hq stay zero
-  v8bf qf[18];
-  {
-    const int r = 16 * hb + c16;
-    const unsigned char* qt = ring + 2 * kTileB;
+  auto issue_tile = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < 18; ++it)
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(offs[it]), "s"(kv_seq),
+                   "{m0}"(ring_base + (i % kNBuf) * kTileB + ((wave - 2) + 2 * it) * 1024));
+  };
+
+  // One loop per role, each with one barrier per step (nt + 1 steps), so that each role's
+  // registers (Q, gather offsets, accumulators) are live only in its own loop.
+  if (role == 0) {
+    v8bf qf[18];                                       // Q of heads 16 wave + c16
+    float m_run = -INFINITY, l_run = 0.f;              // head 16 wave + c16
+    const int r = 16 * wave + c16;
+    const unsigned char* qt = ring + 3 * kTileB;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       qf[ks] = *reinterpret_cast<const v8bf*>(qt + tile_off(r, 4 * ks + g));
       if (h0 + r >= a.Hq) qf[ks] = v8bf{};
     }
+    for (int k = 0; k <= nt; ++k) {
+      lds_barrier();                                   // tile k landed; P of tile k - 1 consumed
+      if (k < nt)
+        score_tile(ring + (k % kNBuf) * kTileB, qf, sidx, k * kKT, nkeys, a.scale_log2, m_run, l_run,
+                   pbuf[k & 1], abuf[k & 1]);
+    }
+    // running max and sum, per head, to the value waves
+    if (g == 0) {
+      fin[0][r] = m_run;
+      fin[1][r] = l_run;
+    }
+    lds_barrier();
+    return;
   }
-  for (int k = 0; k < npairs; ++k) {
-    lds_barrier();                                     // pair k-1 fully consumed (ring slots free)
-    if (k + 1 < npairs) { issue_pair(k + 1); wait_vm<kPairLoads>(); } else { wait_vm<0>(); }
-    lds_barrier();                                     // pair k landed for every thread
-    pair_step(st, ring + ((2 * k) % kNBuf) * kTileB, ring + ((2 * k + 1) % kNBuf) * kTileB, qf,
-              sidx, 2 * k * kKT, nkeys, a.scale_log2, pt, red_max, red_sum);
+  if (role == 1) {
+    tile_offsets(0);
+    issue_tile(0);
+    if (nt > 1) { tile_offsets(1); issue_tile(1); }
+    if (nt > 2) tile_offsets(2);
+    for (int k = 0; k <= nt; ++k) {
+      if (k < nt) {                                    // tile k landed (k + 1 may be in flight)
+        if (k + 1 < nt) wait_vm<18>(); else wait_vm<0>();
+      }
+      lds_barrier();
+      if (k + 2 < nt) {                                // into the slot of tile k - 2
+        issue_tile(k + 2);
+        if (k + 3 < nt) tile_offsets(k + 3);
+      }
+    }
+    lds_barrier();
+    return;
   }
-  const int wave4 = wave;                              // value-dim slice (64 wide) of this wave
+  v4f acc[8][2];                                       // O^T
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) { acc[mb][0] = v4f{0.f, 0.f, 0.f, 0.f}; acc[mb][1] = acc[mb][0]; }
+  for (int k = 0; k <= nt; ++k) {
+    lds_barrier();                                     // P of tile k - 1 published
+    if (k >= 1)
+      value_tile(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1]);
+  }
+  lds_barrier();                                       // running max and sum published
+  const int ow = wave - 4;
 
-  // ---- epilogue: lane holds O^T[d = 64 wave + 16 mb + 4 g + e][head h0 + 16 nb + c16]
+  // ---- epilogue: lane holds O^T[d = 128 ow + 16 mb + 4 g + e][head h0 + 16 nb + c16]
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int h = h0 + 16 * nb + c16;
+    const int hl = 16 * nb + c16;
+    const int h = h0 + hl;
     if (h >= a.Hq) continue;
+    const float mh = fin[0][hl], lh = fin[1][hl];
     if constexpr (FINAL) {
       const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-      const float M = fmaxf(st.m_run[nb], sk);
-      const float f = st.m_run[nb] == -INFINITY ? 0.f : exp2f(st.m_run[nb] - M);
-      const float den = st.l_run[nb] * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
+      const float M = fmaxf(mh, sk);
+      const float f = mh == -INFINITY ? 0.f : exp2f(mh - M);
+      const float den = lh * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
       const float inv = den > 0.f ? f / den : 0.f;
-      u16* orow = a.out + ((long)t * a.Hq + h) * kDv + 64 * wave4 + 4 * g;
+      u16* orow = a.out + ((long)t * a.Hq + h) * kDv + 128 * ow + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 8; ++mb) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][0] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][2] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][3] * inv) << 16);
+        pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
+        pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
         *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
       }
     } else {
       // the split's own softmax average O / l (a convex combination of value rows) in bf16;
       // the merge weighs it by 2^(m - M) l in fp32
       const long base = ((long)t * a.n_split + split) * a.Hq + h;
-      const float inv = st.l_run[nb] > 0.f ? 1.f / st.l_run[nb] : 0.f;
-      u16* orow = a.ws_o + base * kDv + 64 * wave4 + 4 * g;
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      u16* orow = a.ws_o + base * kDv + 128 * ow + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 8; ++mb) {
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][0] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(st.acc_o[mb][nb][2] * inv) | ((uint32_t)f32_to_bf16(st.acc_o[mb][nb][3] * inv) << 16);
+        pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
+        pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
         *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
       }
-      if (wave4 == 0 && g == 0) {
-        a.ws_ml[base * 2 + 0] = st.m_run[nb];
-        a.ws_ml[base * 2 + 1] = st.l_run[nb];
+      if (ow == 0 && g == 0) {
+        a.ws_ml[base * 2 + 0] = mh;
+        a.ws_ml[base * 2 + 1] = lh;
       }
     }
   }
@@ -423,10 +456,10 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
     add(__shfl(f, sp, kWave), *reinterpret_cast<const uint4*>(src + sp * sstride));
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint4 pk;
-  pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
-  pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
-  pk.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
-  pk.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
   *reinterpret_cast<uint4*>(a.out + ((long)t * a.Hq + h) * kDv + lane * 8) = pk;
 }
 
