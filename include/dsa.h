@@ -221,6 +221,50 @@ dsa_status dsa_sparse_attn_merge(const dsa_batch* batch, int32_t Hq, int32_t k,
                                  const float* sink, void* out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* ---------------------------------------------------------------- paged caches ----------- */
+/*
+ * [LI] the Page Attention layout of the caches: a sequence's rows are stored in fixed-size
+ * blocks anywhere in the cache, listed by a block table.  Position p of sequence b lives in
+ * cache row  block_table[b * blocks_per_seq + p / block_size] * block_size + p % block_size
+ * (of k_cache / k_scale for the indexer, of kv for the attention).  The pages use blocks of
+ * 128 rows.  The paged calls take every other argument of their flat counterparts with the
+ * same meaning, results and errors; batch->kv_start is not read (may be NULL).
+ *   block_table     device [num_seqs, blocks_per_seq] int32, entries in [0, num_blocks)
+ *   blocks_per_seq  >= ceil(max_kv_len / block_size); <= 2048 for the attention call (its
+ *                   workgroups stage a sequence's table in on-chip memory)
+ *   block_size      a power of two in [16, 1024]
+ *   num_blocks      physical blocks in the cache; num_blocks * block_size rows must span
+ *                   < 4 GiB of k_cache codes and of kv rows (32-bit gather offsets)
+ * The caller owns the table; entries past a sequence's last block are not read.
+ */
+typedef struct dsa_paging {
+  const int32_t* block_table;
+  int32_t blocks_per_seq;
+  int32_t block_size;
+  int32_t num_blocks;
+} dsa_paging;
+
+/* dsa_indexer_scores with k_cache / k_scale rows addressed through the block table. */
+dsa_status dsa_indexer_scores_paged(const dsa_batch* batch, const dsa_paging* paging, int32_t H,
+                                    int32_t D, dsa_dtype code_dtype, dsa_dtype scale_dtype,
+                                    const void* q_codes, const void* q_scale, const void* w,
+                                    const void* k_cache, const void* k_scale, float* scores,
+                                    int64_t ld, void* stream);
+/* dsa_indexer_topk with k_cache / k_scale rows addressed through the block table. */
+dsa_status dsa_indexer_topk_paged(const dsa_batch* batch, const dsa_paging* paging, int32_t H,
+                                  int32_t D, dsa_dtype code_dtype, dsa_dtype scale_dtype,
+                                  const void* q_codes, const void* q_scale, const void* w,
+                                  const void* k_cache, const void* k_scale, float* scores,
+                                  int64_t ld, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                                  void* stream);
+/* dsa_sparse_attn_decode with kv rows addressed through the block table (kv_row_stride and
+ * the workspace as there). */
+dsa_status dsa_sparse_attn_decode_paged(const dsa_batch* batch, const dsa_paging* paging,
+                                        int32_t Hq, const void* q, const void* kv,
+                                        int64_t kv_row_stride, const int32_t* idx, int32_t k,
+                                        const float* sink, float scale, void* out, void* ws,
+                                        size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- misc -------------------- */
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);

@@ -16,7 +16,8 @@ Sources (cited by page title and section; no line numbers):
   [PRO]   "NPU DeepSeek-V3.2-Exp PyPTO 融合算子开发优化实践" (jsqmd.com/news/787325),
           "Indexer Prolog", formulas and quant strategy.
   [LI]    same page, "Lightning Indexer" (scores -> TopK).
-  [DIA]   same page, "Deepseek Indexer Attention" (the four-part decode layer).
+  [DIA]   same page, "Deepseek Indexer Attention" (the four-part decode layer); the Page
+          Attention cache blocks of the Lightning Indexer analysis (paged.py).
 
 Parity status of each function is stated in its docstring; every function here is
 pinned by CPU tests in tests/test_oracle_*.py except where it says "parity unpinned".
@@ -27,6 +28,7 @@ from .indexer import indexer_dots, indexer_scores
 from .topk import topk_select
 from .sfa import sparse_attention
 from .step import decode_step
+from .paged import paged_rows, flatten_paged
 
 __all__ = ["bf16_encode", "bf16_decode", "e4m3_encode", "e4m3_decode", "fp16_round",
            "hadamard", "apply_rope", "quantize_rows", "prolog_rows", "indexer_prolog",

@@ -26,6 +26,11 @@ class DsaBatch(ctypes.Structure):
                 ("q_pos", ctypes.c_void_p), ("kv_start", ctypes.c_void_p)]
 
 
+class DsaPaging(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("blocks_per_seq", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+
+
 class DsaPrologCfg(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("D", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
                 ("rope_offset", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32),
@@ -39,6 +44,7 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _BP = ctypes.POINTER(DsaBatch)
+_PP = ctypes.POINTER(DsaPaging)
 
 # name -> (restype, argtypes); mirrors include/dsa.h
 SIGNATURES = {
@@ -57,6 +63,12 @@ SIGNATURES = {
     "dsa_sparse_attn_split": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
                                              ctypes.c_float, _P, _P, _SZ, _P]),
     "dsa_sparse_attn_merge": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "dsa_indexer_scores_paged": (ctypes.c_int, [_BP, _PP, _I32, _I32, ctypes.c_int, ctypes.c_int,
+                                                _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "dsa_indexer_topk_paged": (ctypes.c_int, [_BP, _PP, _I32, _I32, ctypes.c_int, ctypes.c_int,
+                                              _P, _P, _P, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_decode_paged": (ctypes.c_int, [_BP, _PP, _I32, _P, _P, _I64, _P, _I32, _P,
+                                                    ctypes.c_float, _P, _P, _SZ, _P]),
     "dsa_last_error": (ctypes.c_char_p, []),
     "dsa_version": (ctypes.c_char_p, []),
 }

@@ -29,6 +29,7 @@ struct IdxArgs {
   float* scores; int32_t* dots; long ld;
   uint32_t* hist; int hist_k;            // optional top-k digit histogram [T][kHistShards][kHistBins]
   int H; int ngrp; int scale_f16; int B; int T;
+  const int32_t* bt; int bps; int bs_log2;   // paged caches: block table (NULL: flat rows)
 };
 
 constexpr int kCK = 512;     // keys per workgroup
@@ -137,10 +138,14 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   // lane vectors in one memory round trip and pick entries by lane; larger ones chain loads.
   int q_lo, q_hi, maxp = -1, p;
   long kv0;
+  // Paged caches: the chunk's physical blocks as a lane vector (block j of the chunk in lane
+  // j), loaded with the metadata; flat caches: the sequence's first row.
+  int bt_l = 0;
+  if (a.bt) bt_l = a.bt[(long)b * a.bps + min((chunk0 >> a.bs_log2) + lane, a.bps - 1)];
   if (a.B < 64 && a.T <= 64) {
     const int qs_l = a.q_start[min(lane, a.B)];
     const int qp_l = a.q_pos[min(lane, a.T - 1)];
-    const long kv_l = a.kv_start[min(lane, a.B - 1)];
+    const long kv_l = a.bt ? 0 : a.kv_start[min(lane, a.B - 1)];
     q_lo = __builtin_amdgcn_readlane(qs_l, b) + g * G;
     q_hi = __builtin_amdgcn_readlane(qs_l, b + 1);
 #pragma unroll
@@ -157,8 +162,15 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     for (int j = 0; j < G; ++j)
       if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
     p = q_lo + ti < q_hi ? a.q_pos[q_lo + ti] : -1;
-    kv0 = a.kv_start[b];
+    kv0 = a.bt ? 0 : a.kv_start[b];
   }
+  // cache row of chunk row r (0 <= r < kCK)
+  auto cache_row = [&](int r) -> long {
+    if (!a.bt) return kv0 + chunk0 + r;
+    const int pos = chunk0 + r;
+    const int blk = __shfl(bt_l, (pos >> a.bs_log2) - (chunk0 >> a.bs_log2), kWave);
+    return ((long)blk << a.bs_log2) + (pos & ((1 << a.bs_log2) - 1));
+  };
   if (q_lo >= q_hi) return;
   if (chunk0 > maxp) return;
   const int t = q_lo + ti;
@@ -219,7 +231,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int r = min((phase + NPH * j) * kBlk + col, last_row);
-      const long row = kv0 + chunk0 + r;
+      const long row = cache_row(r);
       ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
     }
   }
@@ -228,7 +240,10 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   // into the LDS of the last QG key groups, then key group 0.  Q moves on to VGPRs before the
   // remaining key groups are issued.
   const unsigned kl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kl;
-  const uint8_t* kchunk = uniform_ptr(a.k_cache + (kv0 + chunk0) * D);   // DMA base (SGPRs)
+  // DMA base (SGPRs): the chunk's first row (flat) or the cache (paged; rows via the table,
+  // the host checks that the cache spans < 4 GiB)
+  const uint8_t* kchunk = uniform_ptr(a.bt ? a.k_cache : a.k_cache + (kv0 + chunk0) * D);
+  auto chunk_off = [&](int rr) -> uint32_t { return (uint32_t)((a.bt ? cache_row(rr) : (long)rr) * D); };
   {
     const uint8_t* qbase = uniform_ptr(a.q_codes + (long)q_lo * H * D);
     int ln = lane;
@@ -250,7 +265,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     const int r = o / D;
     const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
     const int rr = min(r, last_row);
-    dma16(kchunk, (uint32_t)(rr * D + c * 16), kl_base + j * 1024);
+    dma16(kchunk, chunk_off(rr) + (uint32_t)(c * 16), kl_base + j * 1024);
   }
   idx_wait_vm<EARLY * PER_GROUP>();                      // Q landed (for this wave)
   idx_lds_barrier();                                     // ... and for every wave
@@ -297,7 +312,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     const int r = o / D;
     const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
     const int rr = min(r, last_row);
-    dma16(kchunk, (uint32_t)(rr * D + c * 16), kl_base + j * 1024);
+    dma16(kchunk, chunk_off(rr) + (uint32_t)(c * 16), kl_base + j * 1024);
   }
 
   // ---- consume the groups as they land
@@ -421,12 +436,12 @@ static void launch_g(int G, const IdxArgs& a, dim3 grid, hipStream_t st) {
 
 using dsa_host::fail;
 
-static dsa_status check_batch(const dsa_batch* bt, const char* fn) {
+static dsa_status check_batch(const dsa_batch* bt, const char* fn, bool need_kv = true) {
   if (!bt) return fail(DSA_ERR_INVALID_ARG, "%s: batch is NULL", fn);
   if (bt->num_seqs < 0 || bt->num_q < 0) return fail(DSA_ERR_INVALID_ARG, "%s: negative batch size", fn);
   if (bt->num_q > 0) {
     if (bt->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "%s: tokens without sequences", fn);
-    if (!bt->q_start || !bt->q_seq || !bt->q_pos || !bt->kv_start)
+    if (!bt->q_start || !bt->q_seq || !bt->q_pos || (need_kv && !bt->kv_start))
       return fail(DSA_ERR_INVALID_ARG, "%s: a batch array is NULL", fn);
     if (bt->max_q_per_seq < 1 || bt->max_q_per_seq > bt->num_q)
       return fail(DSA_ERR_INVALID_ARG, "%s: max_q_per_seq out of range (%d)", fn, bt->max_q_per_seq);
@@ -437,13 +452,43 @@ static dsa_status check_batch(const dsa_batch* bt, const char* fn) {
 
 // exported for the other translation units
 dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn) { return check_batch(bt, fn); }
+dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn) { return check_batch(bt, fn, false); }
+
+// A paged layout for batch bt: table present, block size a power of two in [16, 1024], enough
+// blocks per sequence, and num_blocks * block_size rows of row_bytes spanning < 4 GiB.
+// Returns the block size's log2 through bs_log2.
+dsa_status dsa_check_paging(const dsa_paging* pg, const dsa_batch* bt, double row_bytes,
+                            const char* fn, int* bs_log2) {
+  if (!pg) return fail(DSA_ERR_INVALID_ARG, "%s: paging is NULL", fn);
+  const int bs = pg->block_size;
+  if (bs < 16 || bs > 1024 || (bs & (bs - 1)))
+    return fail(DSA_ERR_INVALID_ARG, "%s: block_size must be a power of two in [16, 1024] (got %d)", fn, bs);
+  int l = 0;
+  while ((1 << l) < bs) ++l;
+  *bs_log2 = l;
+  if (bt->num_q == 0) return DSA_OK;
+  if (!pg->block_table) return fail(DSA_ERR_INVALID_ARG, "%s: block_table is NULL", fn);
+  if (pg->num_blocks < 1) return fail(DSA_ERR_INVALID_ARG, "%s: num_blocks must be >= 1", fn);
+  if ((long)pg->blocks_per_seq * bs < bt->max_kv_len)
+    return fail(DSA_ERR_INVALID_ARG, "%s: blocks_per_seq * block_size (%ld) < max_kv_len (%d)", fn,
+                (long)pg->blocks_per_seq * bs, bt->max_kv_len);
+  if ((double)pg->num_blocks * bs * row_bytes >= 4294967296.0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: the paged cache must span < 4 GiB", fn);
+  return DSA_OK;
+}
 
 static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype code, dsa_dtype sdt,
                                  const void* q, const void* qs, const void* w, const void* k,
                                  const void* ks, float* scores, int32_t* dots, bool want_dots,
-                                 long ld, uint32_t* hist, int hist_k, void* stream, const char* fn) {
-  dsa_status st = check_batch(bt, fn);
+                                 long ld, uint32_t* hist, int hist_k, void* stream, const char* fn,
+                                 const dsa_paging* pg = nullptr) {
+  dsa_status st = check_batch(bt, fn, pg == nullptr);
   if (st != DSA_OK) return st;
+  int bs_log2 = 0;
+  if (pg) {
+    st = dsa_check_paging(pg, bt, (double)D, fn, &bs_log2);
+    if (st != DSA_OK) return st;
+  }
   if (!((H == 64 && D == 128) || (H == 8 && D == 64)))
     return fail(DSA_ERR_UNSUPPORTED, "%s: (H, D) = (%d, %d) not compiled; supported (64,128), (8,64)", fn, H, D);
   if (code != DSA_I8 && code != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "%s: code dtype must be I8 or FP8_E4M3", fn);
@@ -461,6 +506,7 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.k_cache = (const uint8_t*)k; a.k_scale = ks; a.scores = scores; a.dots = dots; a.ld = ld;
   a.hist = hist; a.hist_k = hist_k;
   a.H = H; a.scale_f16 = sdt == DSA_F16; a.B = bt->num_seqs; a.T = bt->num_q;
+  if (pg) { a.bt = pg->block_table; a.bps = pg->blocks_per_seq; a.bs_log2 = bs_log2; }
   const int G = bt->max_q_per_seq >= 3 ? 4 : bt->max_q_per_seq;
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
   const long gy = (long)bt->num_seqs * a.ngrp;
@@ -489,14 +535,26 @@ extern "C" dsa_status dsa_indexer_scores(const dsa_batch* batch, int32_t H, int3
                         k_scale, scores, nullptr, false, ld, nullptr, 0, stream, "dsa_indexer_scores");
 }
 
-// Scores plus the fused first radix pass of the top-k (used by dsa_indexer_topk).
+extern "C" dsa_status dsa_indexer_scores_paged(const dsa_batch* batch, const dsa_paging* paging,
+                                               int32_t H, int32_t D, dsa_dtype code_dtype,
+                                               dsa_dtype scale_dtype, const void* q_codes,
+                                               const void* q_scale, const void* w,
+                                               const void* k_cache, const void* k_scale,
+                                               float* scores, int64_t ld, void* stream) {
+  const char* fn = "dsa_indexer_scores_paged";
+  if (!paging) return fail(DSA_ERR_INVALID_ARG, "%s: paging is NULL", fn);
+  return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                        k_scale, scores, nullptr, false, ld, nullptr, 0, stream, fn, paging);
+}
+
+// Scores plus the fused first radix pass of the top-k (used by dsa_indexer_topk[_paged]).
 dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D, dsa_dtype code_dtype,
                                    dsa_dtype scale_dtype, const void* q_codes, const void* q_scale,
                                    const void* w, const void* k_cache, const void* k_scale,
                                    float* scores, int64_t ld, uint32_t* hist, int32_t k,
-                                   void* stream, const char* fn) {
+                                   void* stream, const char* fn, const dsa_paging* paging) {
   return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
-                        k_scale, scores, nullptr, false, ld, hist, k, stream, fn);
+                        k_scale, scores, nullptr, false, ld, hist, k, stream, fn, paging);
 }
 
 extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,

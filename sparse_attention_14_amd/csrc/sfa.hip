@@ -48,7 +48,9 @@ struct SfaArgs {
   const float* sink; float scale_log2;
   u16* out; u16* ws_o; float* ws_ml;
   int T, B, Hq, n_hg, n_split, kps;
+  const int32_t* bt; int bps; int bs_log2;   // paged cache: block table (NULL: flat rows)
 };
+constexpr int kMaxBps = 2048;                        // paged: block-table entries per sequence
 
 
 // Rows are stored unpadded (1152 B) with the 16-byte chunk c of row r at chunk c ^ (r & 7):
@@ -259,22 +261,49 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
     const int j = tid + 512 * u;
     iv[u] = j < nkeys ? a.idx[(long)t * a.k + kbeg + j] : 0;
   }
-  const long kv_lane = a.kv_start[min(lane, a.B - 1)];
+  const long kv_lane = a.bt ? 0 : a.kv_start[min(lane, a.B - 1)];
   const int nkeys_pad = (nkeys + kKT - 1) / kKT * kKT;
+  if (a.bt) {
+    // Paged cache: the sequence's block table goes through ring slot 2 (free until tile 2 is
+    // issued) and the selected positions become cache rows before they are staged.
+    int32_t bv[kMaxBps / 512];
+#pragma unroll
+    for (int u = 0; u < kMaxBps / 512; ++u) {
+      const int j = tid + 512 * u;
+      bv[u] = j < a.bps ? a.bt[(long)seq * a.bps + j] : 0;
+    }
+    int* sbt = reinterpret_cast<int*>(ring + 2 * kTileB);
+#pragma unroll
+    for (int u = 0; u < kMaxBps / 512; ++u) {
+      const int j = tid + 512 * u;
+      if (j < a.bps) sbt[j] = bv[u];
+    }
+    lds_barrier();
+    const int bmask = (1 << a.bs_log2) - 1;
+#pragma unroll
+    for (int u = 0; u < kMaxBps / 512; ++u) {
+      const int ix = iv[u];
+      if (tid + 512 * u < nkeys && ix >= 0)
+        iv[u] = (sbt[min(ix >> a.bs_log2, a.bps - 1)] << a.bs_log2) | (ix & bmask);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < kMaxKps / 512; ++u) {
     const int j = tid + 512 * u;
     if (j < nkeys_pad) sidx[j] = j < nkeys ? iv[u] : -1;
   }
   long kv0;
-  if (a.B <= 64) {
+  if (a.bt) {
+    kv0 = 0;                                           // paged: rows index the whole cache
+  } else if (a.B <= 64) {
     kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_lane >> 32), seq) << 32) |
                  (uint32_t)__builtin_amdgcn_readlane((int)kv_lane, seq));
   } else {
     kv0 = a.kv_start[seq];
   }
-  // DMA addressing: a wave-uniform base (the sequence's first latent row, SGPRs) plus a
-  // 32-bit per-lane byte offset (the host checks that a sequence spans < 4 GiB)
+  // DMA addressing: a wave-uniform base (the sequence's first latent row, or the cache when
+  // paged; SGPRs) plus a 32-bit per-lane byte offset (the host checks that a sequence, or the
+  // paged cache, spans < 4 GiB)
   const u16* kv_seq = uniform_ptr(a.kv + kv0 * a.kv_stride);
   const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
   retire(kv_lane);
@@ -486,6 +515,9 @@ static SfaPlan plan(int T, int Hq, int k) {
 
 using dsa_host::fail;
 dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn);
+dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn);
+dsa_status dsa_check_paging(const dsa_paging* pg, const dsa_batch* bt, double row_bytes,
+                            const char* fn, int* bs_log2);
 
 extern "C" size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int32_t k) {
   if (num_q <= 0 || Hq <= 0 || k <= 0 || Hq % 16) return 0;
@@ -500,9 +532,17 @@ extern "C" size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int3
 static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, const void* kv,
                               int64_t kv_row_stride, const int32_t* idx, int32_t k,
                               const float* sink, float scale, void* out, void* ws, size_t ws_bytes,
-                              const char* fn, dsa::SfaArgs* args, dsa::SfaPlan* plan) {
-  dsa_status st = dsa_check_batch(bt, fn);
+                              const char* fn, dsa::SfaArgs* args, dsa::SfaPlan* plan,
+                              const dsa_paging* pg = nullptr) {
+  dsa_status st = pg ? dsa_check_batch_paged(bt, fn) : dsa_check_batch(bt, fn);
   if (st != DSA_OK) return st;
+  int bs_log2 = 0;
+  if (pg) {
+    st = dsa_check_paging(pg, bt, 2.0 * (double)kv_row_stride, fn, &bs_log2);
+    if (st != DSA_OK) return st;
+    if (bt->num_q > 0 && pg->blocks_per_seq > dsa::kMaxBps)
+      return fail(DSA_ERR_UNSUPPORTED, "%s: blocks_per_seq must be <= %d (got %d)", fn, dsa::kMaxBps, pg->blocks_per_seq);
+  }
   if (Hq != 16 && Hq != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: Hq must be 16 or 128 (got %d)", fn, Hq);
   if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "%s: k must be in [1, 2048] (got %d)", fn, k);
   if (kv_row_stride < dsa::kDqk || kv_row_stride % 8) return fail(DSA_ERR_INVALID_ARG, "%s: kv_row_stride must be >= 576 and a multiple of 8", fn);
@@ -514,7 +554,7 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
   if (need && (!ws || ws_bytes < need)) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
   if (need && ((uintptr_t)ws & 255)) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
-  if ((double)bt->max_kv_len * (double)kv_row_stride * 2.0 >= 4294967296.0)
+  if (!pg && (double)bt->max_kv_len * (double)kv_row_stride * 2.0 >= 4294967296.0)
     return fail(DSA_ERR_UNSUPPORTED, "%s: a sequence's latent rows must span < 4 GiB", fn);
   const long nwg = (long)bt->num_q * p.n_hg * p.n_split;
   if (nwg > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "%s: too many workgroups", fn);
@@ -523,6 +563,7 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   a.kv = (const dsa::u16*)kv; a.kv_stride = kv_row_stride; a.idx = idx; a.k = k; a.sink = sink;
   a.scale_log2 = scale * dsa::kLog2e; a.out = (dsa::u16*)out;
   a.T = bt->num_q; a.B = bt->num_seqs; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
+  if (pg) { a.bt = pg->block_table; a.bps = pg->blocks_per_seq; a.bs_log2 = bs_log2; }
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
     a.ws_o = (dsa::u16*)ws;
@@ -554,6 +595,24 @@ extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, co
   dsa::SfaPlan p{};
   const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
                                     ws_bytes, fn, &a, &p);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_split(a, p, (hipStream_t)stream);
+  sfa_launch_merge(a, p, (hipStream_t)stream);
+  return dsa_host::check_launch(fn);
+}
+
+extern "C" dsa_status dsa_sparse_attn_decode_paged(const dsa_batch* bt, const dsa_paging* paging,
+                                                   int32_t Hq, const void* q, const void* kv,
+                                                   int64_t kv_row_stride, const int32_t* idx,
+                                                   int32_t k, const float* sink, float scale,
+                                                   void* out, void* ws, size_t ws_bytes,
+                                                   void* stream) {
+  const char* fn = "dsa_sparse_attn_decode_paged";
+  if (!paging) return fail(DSA_ERR_INVALID_ARG, "%s: paging is NULL", fn);
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
+                                    ws_bytes, fn, &a, &p, paging);
   if (st != DSA_OK || bt->num_q == 0) return st;
   sfa_launch_split(a, p, (hipStream_t)stream);
   sfa_launch_merge(a, p, (hipStream_t)stream);

@@ -406,6 +406,7 @@ __global__ void __launch_bounds__(kFinNT) topk_finalize(TkArgs a) {
 
 using dsa_host::fail;
 dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn);
+dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn);
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static int tk_nch(int32_t max_kv_len) { return (max_kv_len + dsa::kTkChunk - 1) / dsa::kTkChunk; }
@@ -433,8 +434,9 @@ extern "C" size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int
 // Validates a top-k call and fills the kernel arguments (no launch).
 static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t ld, int32_t k,
                                int32_t* idx, void* ws, size_t ws_bytes, const char* fn,
-                               dsa::TkArgs* out) {
-  dsa_status st = dsa_check_batch(bt, fn);
+                               dsa::TkArgs* out, bool paged = false) {
+  // the top-k reads positions only: a paged batch needs no kv_start
+  dsa_status st = paged ? dsa_check_batch_paged(bt, fn) : dsa_check_batch(bt, fn);
   if (st != DSA_OK) return st;
   if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "%s: k must be in [1, 2048] (got %d)", fn, k);
   if (bt->num_q == 0) return DSA_OK;
@@ -482,7 +484,23 @@ dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D,
                                    dsa_dtype scale_dtype, const void* q_codes, const void* q_scale,
                                    const void* w, const void* k_cache, const void* k_scale,
                                    float* scores, int64_t ld, uint32_t* hist, int32_t k,
-                                   void* stream, const char* fn);
+                                   void* stream, const char* fn, const dsa_paging* paging);
+
+static dsa_status indexer_topk(const dsa_batch* bt, const dsa_paging* pg, int32_t H, int32_t D,
+                               dsa_dtype code_dtype, dsa_dtype scale_dtype, const void* q_codes,
+                               const void* q_scale, const void* w, const void* k_cache,
+                               const void* k_scale, float* scores, int64_t ld, int32_t k,
+                               int32_t* idx, void* ws, size_t ws_bytes, void* stream, const char* fn) {
+  dsa::TkArgs a{};
+  dsa_status st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a, pg != nullptr);
+  if (st != DSA_OK) return st;
+  // the indexer validates its own operands; with no tokens it is a no-op as well
+  st = dsa_indexer_scores_hist(bt, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                               k_scale, scores, ld, bt->num_q ? a.hist : nullptr, k, stream, fn, pg);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  topk_tail(a, (hipStream_t)stream);
+  return dsa_host::check_launch(fn);
+}
 
 extern "C" dsa_status dsa_indexer_topk(const dsa_batch* bt, int32_t H, int32_t D,
                                        dsa_dtype code_dtype, dsa_dtype scale_dtype,
@@ -490,14 +508,19 @@ extern "C" dsa_status dsa_indexer_topk(const dsa_batch* bt, int32_t H, int32_t D
                                        const void* k_cache, const void* k_scale, float* scores,
                                        int64_t ld, int32_t k, int32_t* idx, void* ws,
                                        size_t ws_bytes, void* stream) {
-  const char* fn = "dsa_indexer_topk";
-  dsa::TkArgs a{};
-  dsa_status st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a);
-  if (st != DSA_OK) return st;
-  // the indexer validates its own operands; with no tokens it is a no-op as well
-  st = dsa_indexer_scores_hist(bt, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
-                               k_scale, scores, ld, bt->num_q ? a.hist : nullptr, k, stream, fn);
-  if (st != DSA_OK || bt->num_q == 0) return st;
-  topk_tail(a, (hipStream_t)stream);
-  return dsa_host::check_launch(fn);
+  return indexer_topk(bt, nullptr, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                      k_scale, scores, ld, k, idx, ws, ws_bytes, stream, "dsa_indexer_topk");
+}
+
+extern "C" dsa_status dsa_indexer_topk_paged(const dsa_batch* bt, const dsa_paging* paging,
+                                             int32_t H, int32_t D, dsa_dtype code_dtype,
+                                             dsa_dtype scale_dtype, const void* q_codes,
+                                             const void* q_scale, const void* w,
+                                             const void* k_cache, const void* k_scale,
+                                             float* scores, int64_t ld, int32_t k, int32_t* idx,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_indexer_topk_paged";
+  if (!paging) return fail(DSA_ERR_INVALID_ARG, "%s: paging is NULL", fn);
+  return indexer_topk(bt, paging, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+                      k_scale, scores, ld, k, idx, ws, ws_bytes, stream, fn);
 }

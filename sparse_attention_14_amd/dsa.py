@@ -14,7 +14,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (DSA_BF16, DSA_F16, DSA_F32, DSA_FP8_E4M3, DSA_I8, DsaBatch, DsaPrologCfg,
+from ._lib import (DSA_BF16, DSA_F16, DSA_F32, DSA_FP8_E4M3, DSA_I8, DsaBatch, DsaPaging, DsaPrologCfg,
                    check, lib)
 
 D_QK, D_V = 576, 512
@@ -121,6 +121,22 @@ def dsa_indexer_prolog(H: int, D: int, code: str, scale_dt: str, *, q_in=None, q
         ctypes.byref(cfg), nq, _ptr(q_in), _ptr(q_cos), _ptr(q_sin), _ptr(q_codes), _ptr(q_scale),
         nk, _ptr(k_in), _ptr(k_cos), _ptr(k_sin), _ptr(k_slot), _ptr(k_cache), _ptr(k_scale),
         _stream()))
+
+
+@dataclass
+class Paging:
+    """A paged cache layout (mirrors dsa_paging): position p of sequence b is cache row
+    block_table[b, p // block_size] * block_size + p % block_size."""
+    block_table: torch.Tensor  # [B, blocks_per_seq] int32
+    block_size: int
+    num_blocks: int
+
+    def c(self) -> DsaPaging:
+        _need(self.block_table, "block_table", torch.int32)
+        if self.block_table.dim() != 2:
+            raise ValueError("block_table must be [B, blocks_per_seq]")
+        return DsaPaging(self.block_table.data_ptr(), self.block_table.shape[1], self.block_size,
+                         self.num_blocks)
 
 
 def _scores_ld(max_kv_len: int) -> int:
@@ -286,6 +302,73 @@ def dsa_sparse_attn_merge(batch: Batch, Hq: int, k: int, sink: Optional[torch.Te
     b = batch.c()
     check("dsa_sparse_attn_merge", lib.dsa_sparse_attn_merge(
         ctypes.byref(b), Hq, k, _ptr(sink), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream()))
+    return out
+
+
+def _indexer_operands(batch, H, D, code, scale_dt, q_codes, q_scale, w, k_cache, k_scale, scores):
+    T = batch.num_q
+    ct, st = _CODE_TORCH[code], _SCALE_TORCH[scale_dt]
+    _need(q_codes, "q_codes", ct, (T, H, D))
+    _need(q_scale, "q_scale", st, (T, H))
+    _need(w, "w", torch.float16, (T, H))
+    _need(k_cache, "k_cache", ct)
+    _need(k_scale, "k_scale", st)
+    if scores is None:
+        scores = torch.empty((T, _scores_ld(batch.max_kv_len)), dtype=torch.float32,
+                             device=q_codes.device)
+    _need(scores, "scores", torch.float32)
+    return scores
+
+
+def dsa_indexer_scores_paged(batch: Batch, paging: Paging, H: int, D: int, code: str,
+                             scale_dt: str, q_codes, q_scale, w, k_cache, k_scale,
+                             scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dsa_indexer_scores with k_cache / k_scale rows addressed through the block table."""
+    scores = _indexer_operands(batch, H, D, code, scale_dt, q_codes, q_scale, w, k_cache, k_scale,
+                               scores)
+    b, pg = batch.c(), paging.c()
+    check("dsa_indexer_scores_paged", lib.dsa_indexer_scores_paged(
+        ctypes.byref(b), ctypes.byref(pg), H, D, _CODE[code], _SCALE[scale_dt], _ptr(q_codes),
+        _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+        scores.shape[1] if scores.dim() == 2 else 0, _stream()))
+    return scores
+
+
+def dsa_indexer_topk_paged(batch: Batch, paging: Paging, H: int, D: int, code: str,
+                           scale_dt: str, q_codes, q_scale, w, k_cache, k_scale, k: int,
+                           scores: Optional[torch.Tensor] = None,
+                           idx: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dsa_indexer_topk with k_cache / k_scale rows addressed through the block table."""
+    T = batch.num_q
+    scores = _indexer_operands(batch, H, D, code, scale_dt, q_codes, q_scale, w, k_cache, k_scale,
+                               scores)
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_codes.device)
+    _need(idx, "idx", torch.int32, (T, k))
+    if ws is None:
+        ws = _workspace(dsa_topk_workspace_size(T, batch.max_kv_len, k), q_codes.device)
+    _need(ws, "ws", torch.uint8)
+    b, pg = batch.c(), paging.c()
+    check("dsa_indexer_topk_paged", lib.dsa_indexer_topk_paged(
+        ctypes.byref(b), ctypes.byref(pg), H, D, _CODE[code], _SCALE[scale_dt], _ptr(q_codes),
+        _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+        scores.shape[1] if scores.dim() == 2 else 0, k, _ptr(idx), _ptr(ws), ws.numel(),
+        _stream()))
+    return idx
+
+
+def dsa_sparse_attn_decode_paged(batch: Batch, paging: Paging, q: torch.Tensor, kv: torch.Tensor,
+                                 idx: torch.Tensor, sink: Optional[torch.Tensor], scale: float,
+                                 out: Optional[torch.Tensor] = None,
+                                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dsa_sparse_attn_decode with kv rows addressed through the block table."""
+    Hq, k, out, ws = _sfa_args(batch, q, kv, idx, sink, out, ws)
+    b, pg = batch.c(), paging.c()
+    check("dsa_sparse_attn_decode_paged", lib.dsa_sparse_attn_decode_paged(
+        ctypes.byref(b), ctypes.byref(pg), Hq, _ptr(q), _ptr(kv), kv.stride(0), _ptr(idx), k,
+        _ptr(sink), ctypes.c_float(scale), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream()))
     return out
 

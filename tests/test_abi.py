@@ -122,3 +122,40 @@ def test_binding_rejects_cpu_tensors():
     from sparse_attention_14_amd import dsa
     with pytest.raises(ValueError):
         dsa._need(torch.zeros(3), "x", torch.float32)
+
+
+def test_paged_validation_before_any_device_call():
+    L = _lib()
+    lib = L.lib
+    b = _batch()
+    P = ctypes.c_void_p(0x1000)
+    PP = lambda bs=128, bps=512, nb=2048, tab=P: L.DsaPaging(tab, bps, bs, nb)
+    big = 1 << 30
+    # NULL paging
+    assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(b), None, 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, P, big, None) == L.DSA_ERR_INVALID_ARG
+    assert b"paging is NULL" in lib.dsa_last_error()
+    assert lib.dsa_indexer_topk_paged(ctypes.byref(b), None, 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, 2048, P, P, big, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores_paged(ctypes.byref(b), None, 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    # block size not a power of two / out of range
+    for bs in (100, 8, 2048):
+        pg = PP(bs=bs)
+        assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(b), ctypes.byref(pg), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, P, big, None) == L.DSA_ERR_INVALID_ARG
+        assert lib.dsa_indexer_scores_paged(ctypes.byref(b), ctypes.byref(pg), 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    # too few blocks per sequence for max_kv_len (65536), NULL table, no blocks
+    for pg in (PP(bps=100), PP(tab=None), PP(nb=0)):
+        assert lib.dsa_indexer_topk_paged(ctypes.byref(b), ctypes.byref(pg), 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 65536, 2048, P, P, big, None) == L.DSA_ERR_INVALID_ARG
+    # the attention stages at most 2048 table entries per sequence; caches must span < 4 GiB
+    pg = PP(bs=16, bps=4096)
+    assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(b), ctypes.byref(pg), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, P, big, None) == L.DSA_ERR_UNSUPPORTED
+    pg = PP(nb=1 << 20)
+    assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(b), ctypes.byref(pg), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, P, big, None) == L.DSA_ERR_UNSUPPORTED
+    # a paged batch may leave kv_start NULL; an empty one is a no-op
+    nb = _batch()
+    nb.kv_start = None
+    pg = PP(bps=100)
+    assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(nb), ctypes.byref(pg), 128, P, P, 576, P, 2048, None, ctypes.c_float(0.04), P, P, big, None) == L.DSA_ERR_INVALID_ARG
+    assert b"blocks_per_seq" in lib.dsa_last_error()
+    e = _batch(T=0, B=0, mq=0, ml=0)
+    pg = PP()
+    assert lib.dsa_indexer_topk_paged(ctypes.byref(e), ctypes.byref(pg), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, 2048, None, None, 0, None) == L.DSA_OK
+    assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(e), ctypes.byref(pg), 128, None, None, 576, None, 2048, None, ctypes.c_float(0.04), None, None, 0, None) == L.DSA_OK

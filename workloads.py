@@ -198,6 +198,36 @@ def random_topk_idx(rng: np.random.Generator, q_pos: np.ndarray, k: int,
     return out
 
 
+@dataclasses.dataclass
+class BlockLayout:
+    """A paged placement of a workload's flat caches (rows of sequence b at kv_start[b] + p):
+    sequence b's logical block j sits in physical block table[b, j]; row_map[r] is the paged
+    row of flat row r.  Pure data layout: blocks of `block_size` rows in a random order, with
+    `spare` unused blocks mixed in."""
+    block_size: int
+    table: np.ndarray        # [B, blocks_per_seq] int32 (-1 past a sequence's last block)
+    row_map: np.ndarray      # [N] int64
+    num_blocks: int
+
+
+def block_layout(wl: Workload, block_size: int, seed: int = 0, spare: int = 3) -> BlockLayout:
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in wl.seq_lens]
+    nblk = [-(-n // block_size) for n in lengths]
+    total = sum(nblk) + spare
+    perm = rng.permutation(total)
+    table = np.full((len(lengths), max(nblk)), -1, dtype=np.int32)
+    row_map = np.empty(wl.N, dtype=np.int64)
+    k = 0
+    for b, n in enumerate(lengths):
+        for j in range(nblk[b]):
+            table[b, j] = perm[k]
+            k += 1
+        p = np.arange(n)
+        row_map[int(wl.kv_start[b]) + p] = table[b, p // block_size].astype(np.int64) * block_size + p % block_size
+    return BlockLayout(block_size, table, row_map, total)
+
+
 def device_arrays(wl: Workload, device="cuda") -> dict:
     """The same workload as torch tensors on `device` (no arithmetic: copies and dtype views)."""
     import torch
