@@ -250,9 +250,46 @@ def main():
     wall = time.perf_counter() - t0
     us_step = e0.elapsed_time(e1) * 1000.0 / K
 
+    # paged caches (Page Attention blocks of 128 rows, shuffled): copies of every set's K and
+    # KV caches, for the paged calls' stage timing; they must select and attend exactly as the
+    # flat calls do
+    lay = workloads.block_layout(wl, 128, seed=1)
+    rm = torch.as_tensor(lay.row_map, device=dev)
+    rows_p = lay.num_blocks * 128
+    paging = dsa.Paging(torch.as_tensor(lay.table, device=dev), 128, lay.num_blocks)
+
+    def paged_copy(t):
+        out = torch.zeros((rows_p,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+        out[rm] = t
+        return out
+
+    for s in sets:
+        s.k_cache_p, s.k_scale_p, s.kv_p = paged_copy(s.k_cache), paged_copy(s.k_scale), paged_copy(s.kv)
+
+    def st_indexer_topk_paged(s):
+        dsa.dsa_indexer_topk_paged(batch, paging, H, D, cfg.code, cfg.scale_dt, s.buf.q_codes,
+                                   s.buf.q_scale, s.w, s.k_cache_p, s.k_scale_p, k,
+                                   scores=s.buf.scores, idx=s.buf.idx, ws=s.buf.ws_topk)
+
+    def st_sfa_paged(s):
+        dsa.dsa_sparse_attn_decode_paged(batch, paging, s.q, s.kv_p, s.buf.idx, sink, wl.scale,
+                                         out=s.buf.out, ws=s.buf.ws_sfa)
+
+    with torch.cuda.stream(stream):
+        st_indexer_topk(sets[0])
+        idx_flat = sets[0].buf.idx.clone()
+        st_sfa(sets[0])
+        out_flat = sets[0].buf.out.clone()
+        st_indexer_topk_paged(sets[0])
+        st_sfa_paged(sets[0])
+    torch.cuda.synchronize()
+    assert torch.equal(sets[0].buf.idx, idx_flat) and torch.equal(sets[0].buf.out, out_flat), \
+        "paged calls differ from flat"
+
     # per-stage / per-kernel timing: R launches of one stage per graph replay
     stages = {"prolog": st_prolog, "indexer": st_indexer, "indexer_topk": st_indexer_topk,
-              "sfa": st_sfa, "sfa_split": st_sfa_split, "sfa_merge": st_sfa_merge}
+              "sfa": st_sfa, "sfa_split": st_sfa_split, "sfa_merge": st_sfa_merge,
+              "indexer_topk_paged": st_indexer_topk_paged, "sfa_paged": st_sfa_paged}
     stage_us = {}
     for name, fn in stages.items():
         g = capture(fn)
