@@ -155,10 +155,10 @@ dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
  * order-preserving keys; -0.0 equals +0.0).  1 <= k <= 2048.
  *   scores device [T, ld] fp32 (as written by dsa_indexer_scores), idx device [T, k] int32.
  *   ws: device workspace of at least dsa_topk_workspace_size(T, max_kv_len, k) bytes,
- *       256-byte aligned, ZERO-FILLED before its first use; every call leaves the parts that
- *       must start at zero (per-row histograms, position bitmaps, counters) zeroed again, so
- *       a workspace is allocated and cleared once and then reused.  Calls sharing a workspace
- *       must not overlap.  max_kv_len <= 262144.
+ *       256-byte aligned, ZERO-FILLED before its first use; every call leaves the part that
+ *       must start at zero (the per-row histograms) zeroed again, so a workspace is allocated
+ *       and cleared once and then reused.  Calls sharing a workspace must not overlap.
+ *       max_kv_len <= 262144.
  */
 size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k);
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,

@@ -8,12 +8,12 @@
 //   I[t,s] = k_scale[s] * sum_h (w * q_scale)[t,h] * max(D[t,h,s], 0),  D = q[t,h,:] . k[s,:]
 //
 // Work decomposition (decode and prefill shapes alike): a workgroup owns one sequence, a group
-// of G of its query tokens and a chunk of CK = 512 cached keys.  Its 4 waves split the chunk's
+// of G of its query tokens and a chunk of CK = 512 cached keys.  Its waves split the chunk's
 // 32-key blocks; a wave keeps one token's query codes (all heads) resident in VGPRs as the MFMA
-// A operand and streams key rows straight from HBM into VGPRs as the B operand -- every key
-// byte is read from HBM once per token group, with no LDS round trip.  The head reduction is
-// fused: the 32x32 accumulator puts 16 heads of one key in a lane and the other 16 in lane
-// l^32, so the weighted ReLU sum is 16 FMAs per M-block plus a single cross-lane add.
+// A operand and reads key rows from LDS as the B operand (the chunk moves HBM -> LDS once per
+// token group with direct loads).  The head reduction is fused: the 32x32 accumulator puts 16
+// heads of one key in a lane and the other 16 in lane l^32, so the weighted ReLU sum is 16
+// FMAs per M-block plus a single cross-lane add.
 //
 // MFMA k-permutation: the contraction runs over all D dims, so A and B only need the same
 // (lane, byte) -> d assignment.  Lane half hv = lane/32 owns dims [hv*D/2, hv*D/2 + D/2) of
@@ -118,15 +118,33 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, unsigned l
 constexpr int kGroups = 4;                    // 128-key groups per chunk
 
 // G = query tokens per workgroup (1, 2, 4); NMB = 32-head M-blocks per token (ceil(H/32)).
+// Waves per workgroup (four: each 32-key block of a 128-key group goes to one wave per token
+// pair; eight waves were measured no faster, the kernel being bound by its memory phases).
+template <int G>
+struct IdxWaves { static constexpr int value = 4; };
+
 template <int G, int NMB, int D, bool FP8, bool DOTS, bool SF16>
-__global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
-  constexpr int NPH = 4 / G;                 // waves sharing one token
+__global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArgs a) {
+  constexpr int NW = IdxWaves<G>::value;
+  constexpr int NT = NW * 64;
+  constexpr int NPH = NW / G;                // waves sharing one token
   constexpr int CPR = D / 16;                // 16-byte chunks per key row
   constexpr int KB = kCK * D;                // chunk bytes in LDS
   constexpr int INSTR = KB / 1024;           // DMA wave-instructions for the chunk
-  constexpr int PER_GROUP = INSTR / 4 / kGroups;   // per thread per group
-  __shared__ __attribute__((aligned(1024))) unsigned char kl[KB];
-  __shared__ float scl[DOTS ? 1 : G][kCK];                              // scores of the chunk
+  constexpr int PER_GROUP = INSTR / NW / kGroups;  // per thread per group
+  constexpr int HT = D == 128 ? 64 : 8;                  // indexer heads of the compiled shape
+  constexpr int QB = G * HT * D;                         // the group's query codes (bytes)
+  constexpr int GB = kCK / kGroups * D;                  // one key group in LDS (bytes)
+  constexpr int QG = QB <= GB ? 1 : QB / GB;             // key groups whose LDS holds Q first
+  // Decode shapes (Q of the group <= 16 KiB): Q gets an LDS region of its own, which the
+  // chunk's scores reuse once Q sits in VGPRs (80 KiB in all: two workgroups per CU), and every
+  // key group is issued together with Q -- one memory round trip for all operands.  Larger
+  // groups (prefill) stage Q in the last key groups' LDS and issue those groups after Q moved.
+  constexpr bool SEPQ = QB <= 16384;
+  constexpr int QR = SEPQ ? (QB > G * kCK * 4 ? QB : G * kCK * 4) : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char kl[KB + QR];
+  __shared__ float scl_s[(DOTS || SEPQ) ? 1 : G][kCK];
+  float (*scl)[kCK] = SEPQ ? reinterpret_cast<float (*)[kCK]>(kl + KB) : scl_s;   // scores of the chunk
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hv = lane >> 5, col = lane & 31;
@@ -181,16 +199,13 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   // behind a per-element branch is issued and waited for one at a time.
   const int tc = live ? t : q_hi - 1;
   const int nvalid = min(G, q_hi - q_lo);                // query tokens of this group
-  constexpr int HT = D == 128 ? 64 : 8;                  // indexer heads of the compiled shape
-  constexpr int QB = G * HT * D;                         // the group's query codes (bytes)
-  constexpr int GB = kCK / kGroups * D;                  // one key group in LDS (bytes)
-  constexpr int QG = QB <= GB ? 1 : QB / GB;             // key groups whose LDS holds Q first
-  constexpr int QI = (QB + 4095) / 4096;                 // Q loads per wave (1 KiB each)
+  constexpr int QI = (QB + NW * 1024 - 1) / (NW * 1024); // Q loads per wave (1 KiB each)
   constexpr int QJ = QB >= 1024 ? QB / 1024 : 1;         // Q loads in all
   // key group 0 travels with Q; groups 1.. are issued once Q sits in VGPRs (the last QG of
   // them overwrite Q's LDS) and land while the earlier groups are being consumed
-  constexpr int EARLY = 1;
-  static_assert(EARLY + QG <= kGroups, "Q staging overlaps the first key group");
+  constexpr int EARLY = SEPQ ? kGroups : 1;
+  constexpr unsigned QOFF = SEPQ ? KB : (kGroups - QG) * GB;   // Q's LDS offset
+  static_assert(SEPQ || EARLY + QG <= kGroups, "Q staging overlaps the first key group");
   static_assert(QB <= QG * GB && QB % 1024 == 0 || QB < 1024, "Q staging does not fit");
   // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane:
   // rows 8 j + 4 hv + e (e < 4) of the block are four consecutive heads, one 8-byte load of w
@@ -250,17 +265,17 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int it = 0; it < QI; ++it) {
-      const int j = min(wave + 4 * it, QJ - 1);
+      const int j = min(wave + NW * it, QJ - 1);
       const int o = j * 1024 + ln * 16;
       const int r = o / D;                                 // token * HT + head
       const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
       const int tok = min(r / HT, nvalid - 1);
-      dma16(qbase, (uint32_t)((tok * HT + r % HT) * D + c * 16), kl_base + (kGroups - QG) * GB + j * 1024);
+      dma16(qbase, (uint32_t)((tok * HT + r % HT) * D + c * 16), kl_base + QOFF + j * 1024);
     }
   }
 #pragma unroll
   for (int it = 0; it < EARLY * PER_GROUP; ++it) {
-    const int j = wave + 4 * it;
+    const int j = wave + NW * it;
     const int o = j * 1024 + lane * 16;
     const int r = o / D;
     const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
@@ -273,7 +288,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int r = ti * HT + min(32 * mb + col, H - 1);
-    const unsigned char* qrow = kl + (kGroups - QG) * GB + r * D;
+    const unsigned char* qrow = kl + QOFF + r * D;
 #pragma unroll
     for (int q = 0; q < CPR / 2; ++q) {
       const int cc = hv * (CPR / 2) + q;
@@ -291,7 +306,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
     }
   }
   // retire every compiler-visible load (the early key groups land with them), and let every
-  // wave finish reading Q before the last groups overwrite its LDS
+  // wave finish reading Q before the last groups (or the scores) overwrite its LDS
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -306,8 +321,8 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
   }
   idx_lds_barrier();
 #pragma unroll
-  for (int it = EARLY * PER_GROUP; it < INSTR / 4; ++it) {
-    const int j = wave + 4 * it;
+  for (int it = EARLY * PER_GROUP; it < INSTR / NW; ++it) {
+    const int j = wave + NW * it;
     const int o = j * 1024 + lane * 16;
     const int r = o / D;
     const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
@@ -390,7 +405,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
       const int pj = a.q_pos[tj];
       const int n = min(kCK, pj + 1 - chunk0);
       float* dst = a.scores + (long)tj * a.ld + chunk0;
-      for (int e = threadIdx.x; e < n; e += 256) dst[e] = scl[j][e];
+      for (int e = threadIdx.x; e < n; e += NT) dst[e] = scl[j][e];
     }
     if (a.hist) {
       // The top-k's first radix pass, fused: histogram of the top 11 key bits of this chunk's
@@ -398,7 +413,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
       // token's histogram shards.  Rows with at most hist_k valid keys get no histogram.
       uint32_t* hl = reinterpret_cast<uint32_t*>(kl);
       static_assert(G * kHistBins * 4 <= KB, "histogram does not fit the key buffer");
-      for (int i = threadIdx.x; i < G * kHistBins; i += 256) hl[i] = 0u;
+      for (int i = threadIdx.x; i < G * kHistBins; i += NT) hl[i] = 0u;
       __syncthreads();
       for (int j = 0; j < G; ++j) {
         const int tj = q_lo + j;
@@ -406,10 +421,10 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
         const int pj = a.q_pos[tj];
         if (pj + 1 <= a.hist_k) continue;
         const int n = min(kCK, pj + 1 - chunk0);
-        for (int e = threadIdx.x; e < n; e += 256) atomicAdd(&hl[j * kHistBins + (order_key(scl[j][e]) >> 21)], 1u);
+        for (int e = threadIdx.x; e < n; e += NT) atomicAdd(&hl[j * kHistBins + (order_key(scl[j][e]) >> 21)], 1u);
       }
       __syncthreads();
-      for (int i = threadIdx.x; i < G * kHistBins; i += 256) {
+      for (int i = threadIdx.x; i < G * kHistBins; i += NT) {
         const int j = i / kHistBins;
         const uint32_t c = hl[i];
         if (c && q_lo + j < q_hi)
@@ -421,8 +436,9 @@ __global__ void __launch_bounds__(256) indexer_kernel(IdxArgs a) {
 
 template <int G, int NMB, int D, bool FP8, bool DOTS>
 static void launch(const IdxArgs& a, dim3 grid, hipStream_t st) {
-  if (a.scale_f16) hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, false>), grid, dim3(256), 0, st, a);
+  const dim3 block(IdxWaves<G>::value * 64);
+  if (a.scale_f16) hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((indexer_kernel<G, NMB, D, FP8, DOTS, false>), grid, block, 0, st, a);
 }
 
 template <int NMB, int D, bool FP8, bool DOTS>

@@ -2,20 +2,24 @@
 //
 // [LI] "Lightning Indexer" (jsqmd.com/news/787325): the indexer ends in a TopK; the page
 // points at its single-core sort-and-merge tail at batch 4 and proposes sorting inside the
-// preceding vector stage and merging at the end.  Here a row is split across many
-// workgroups instead, so a decode batch of 8 rows still spreads over the whole chip:
+// preceding vector stage and merging at the end.  Here every stage spreads a row over many
+// workgroups, so a decode batch of 8 rows still occupies the whole chip:
 //
 //   hist    : the top 11 bits of every key, per row, in a 2048-bin histogram (its own pass,
 //             or fused into the indexer workgroups by dsa_indexer_topk)
-//   select  : one workgroup per 4096-score chunk re-derives the digit b1 that holds the k-th
-//             largest key; positions above b1 go into the row's position bitmap, positions
-//             with digit b1 (candidates) into the row's candidate list
-//   finalize: one workgroup per row resolves the exact k-th key K* with two more digits over
-//             the candidates, adds the candidates above K* (and the lowest-position ties at
-//             K*) to the bitmap and writes its set positions in order: ascending output with
-//             no sort, ties to the lower position.  (A last-workgroup-finalizes scheme inside
-//             the select pass needs a device-scope release per workgroup, which writes back
-//             the L2 and costs more than the extra launch.)
+//   select  : one workgroup per 4096-score chunk derives the digit b1 that holds the k-th
+//             largest key; positions above b1 go into the chunk's position bitmap, positions
+//             with digit b1 (candidates, 1-3 % of a Gaussian-like row) into the chunk's
+//             candidate list
+//   finalize: again one workgroup per chunk.  Each one loads every candidate of its row and
+//             resolves the exact k-th key K* with two more digits (the same answer in every
+//             workgroup), counts what the earlier chunks contribute to the selection, and
+//             writes its own chunk's selected positions at that offset: ascending output with
+//             no sort and no cross-workgroup exchange, ties to the lower position.
+// A workgroup's work is a short instruction stream after one memory round trip; the
+// alternatives (one workgroup per row, or device-scope fences between workgroups) cost
+// several microseconds of issue time or L2 write-back on this part.  Rows whose candidate
+// lists overflow (near-constant scores, massive ties) resolve K* by streaming the row again.
 //
 // [SFA] step 2: slots past the selection are -1.  Keys: fp32 bits, sign-flipped so that
 // unsigned order equals numeric order; -0.0 is mapped to +0.0 first.
@@ -27,22 +31,23 @@ namespace dsa {
 
 constexpr int kBins = kHistBins;     // 11-bit digits
 constexpr int kShards = kHistShards; // copies of each row histogram (spread atomic traffic)
-constexpr int kTkChunk = 4096;       // scores per select workgroup
-constexpr int kTkNT = 256;           // threads per select workgroup
-constexpr int kPerThr = kTkChunk / kTkNT;
-constexpr int kSlotCap = 256;        // entries per (chunk, wave) slot
+constexpr int kNT = 1024;            // threads per workgroup
+constexpr int kChunk = 4 * kNT;      // scores per chunk: one float4 per thread
+constexpr int kCW = kChunk / 32;     // bitmap words per chunk
+constexpr int kMaxLen = 64 * kChunk; // longest row
+constexpr int kCap = 512;            // candidate slots per chunk
+constexpr int kLoadC = 4;            // candidate entries per finalize thread (first trip)
 
 // Workspace (zero-filled before the first call; every call leaves the histograms zero-filled
 // again, and the rest is written before it is read):
-//   hist  [T][kShards][kBins] u32          row histogram of the top digit, in shards
-//   cnt   [T][nch][4] u32                  per (chunk, wave): n_above | n_cand << 16
-//   b1    [T] u32                          the row's threshold digit
-//   bits  [T][bw] u32                      per row: bitmap of the positions above b1
-//   slots [T][nch][4][kSlotCap] u64        per (chunk, wave): candidates, key << 32 | position
+//   hist  [T][kShards][kBins] u32   row histogram of the top digit
+//   bg    [T][2] u32                the row's threshold digit b1 and the count above it
+//   cnt   [T][nch] u32              per chunk: n_above | n_cand << 16
+//   bits  [T][nch][kCW] u32         per chunk: positions above b1
+//   slots [T][nch][kCap] u64        per chunk: candidates, key << 32 | position
 struct TkArgs {
   const int32_t* q_pos; const float* scores; long ld; int k; int T; int nch;
-  int32_t* idx; uint32_t* hist; uint32_t* cnt; uint32_t* b1; uint32_t* bits; long bw;
-  uint64_t* slots;
+  int32_t* idx; uint32_t* hist; uint32_t* bg; uint32_t* cnt; uint32_t* bits; uint64_t* slots;
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave: four row shifts within each 16-lane row,
@@ -96,310 +101,254 @@ __device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* s
   __syncthreads();
 }
 
+// This thread's four scores of chunk ch (positions ch * kChunk + 4 tid .. +3); every address
+// lies inside the row's ld columns, positions past p are masked by the caller.
+__device__ __forceinline__ float4 load4(const float* row, long ld, int ch) {
+  const long e0 = min((long)ch * kChunk + 4 * threadIdx.x, (ld & ~3L) - 4);
+  return *reinterpret_cast<const float4*>(row + e0);
+}
+
 // First pass (when the indexer did not accumulate it): histogram of the top 11 key bits of a
-// 4096-score chunk in LDS; non-zero bins are added to shard (chunk % kShards) of the row's.
-__global__ void __launch_bounds__(kTkNT) topk_hist(TkArgs a) {
+// chunk in LDS; non-zero bins are added to shard (chunk % kShards) of the row's.
+__global__ void __launch_bounds__(kNT) topk_hist(TkArgs a) {
   __shared__ uint32_t h[kBins];
-  const int t = blockIdx.y;
+  const int t = blockIdx.y, ch = blockIdx.x;
   const int p = a.q_pos[t];
-  if (p + 1 <= a.k) return;
-  const long s0 = (long)blockIdx.x * kTkChunk;
-  if (s0 > p) return;
-  for (int i = threadIdx.x; i < kBins; i += kTkNT) h[i] = 0u;
+  const float4 v = load4(a.scores + (long)t * a.ld, a.ld, ch);
+  if (p + 1 <= a.k || ch * kChunk > p) return;
+  for (int i = threadIdx.x; i < kBins; i += kNT) h[i] = 0u;
   __syncthreads();
-  const float* row = a.scores + (long)t * a.ld + s0;
-  const int n = (int)min((long)kTkChunk, (long)p + 1 - s0);
-  float4 vv[kPerThr / 4];                                 // all loads first (in-bounds; masked)
+  const int e0 = ch * kChunk + 4 * threadIdx.x;
+  const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int j = 0; j < kPerThr / 4; ++j) {
-    const int e0 = min(threadIdx.x * 4 + j * kTkNT * 4, (int)(((a.ld - s0) & ~3L) - 4));
-    vv[j] = *reinterpret_cast<const float4*>(row + e0);
-  }
-#pragma unroll
-  for (int j = 0; j < kPerThr / 4; ++j) {
-    const int e0 = threadIdx.x * 4 + j * kTkNT * 4;
-    const float e[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (e0 + q < n) atomicAdd(&h[order_key(e[q]) >> 21], 1u);
-  }
+  for (int q = 0; q < 4; ++q)
+    if (e0 + q <= p) atomicAdd(&h[order_key(f[q]) >> 21], 1u);
   __syncthreads();
-  uint32_t* gh = a.hist + ((long)t * kShards + blockIdx.x % kShards) * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kTkNT)
+  uint32_t* gh = a.hist + ((long)t * kShards + ch % kShards) * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kNT)
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Select pass: one workgroup per 4096-score chunk.  From the row histogram it re-derives the
-// top digit b1 that holds the k-th largest key.  Positions with digit > b1 are certainly
-// selected: each thread stores the 16-bit mask of its 16 positions into the row's position
-// bitmap (every call rewrites the chunk's bits, so the bitmap needs no clearing).  Positions
-// with digit == b1 are candidates: each wave writes them (key, position) to its own slot (wave
-// prefix sum, no atomics).
-__global__ void __launch_bounds__(kTkNT) topk_select(TkArgs a) {
+// Select: one workgroup per chunk.  One memory round trip (q_pos, the row histogram and the
+// chunk's scores), the threshold digit b1 from the histogram, then the chunk's bitmap of
+// positions above b1 and its candidates (digit == b1) in position order (block scan).
+__global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
   __shared__ uint32_t h[kBins];
-  __shared__ uint32_t sh[kTkNT / 64];
+  __shared__ uint32_t sh[kNT / 64];
   __shared__ uint32_t res[2];
-  const int t = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ch = blockIdx.x;
-  const long s0 = (long)ch * kTkChunk;                    // < ld: the grid covers max_kv_len
-  const float* row = a.scores + (long)t * a.ld + s0;
-  // the chunk's scores, the row histogram and q_pos are loaded together (one memory round
-  // trip; every address is in bounds whatever the row's length)
+  __shared__ uint32_t bw[kCW];
+  const int t = blockIdx.y, ch = blockIdx.x;
+  const int tid = threadIdx.x;
   const int p = a.q_pos[t];
-  float4 vv[kPerThr / 4];
-#pragma unroll
-  for (int j = 0; j < kPerThr / 4; ++j) {                // thread owns 16 consecutive scores
-    const int e0 = min(tid * kPerThr + 4 * j, (int)(((a.ld - s0) & ~3L) - 4));
-    vv[j] = *reinterpret_cast<const float4*>(row + e0);   // in-bounds; masked below
-  }
+  const float4 v = load4(a.scores + (long)t * a.ld, a.ld, ch);
   const uint32_t* gh = a.hist + (long)t * kShards * kBins;
-  uint32_t hv[kShards][kBins / kTkNT];
+  uint32_t hv[kShards][kBins / kNT];
 #pragma unroll
   for (int sd = 0; sd < kShards; ++sd)
 #pragma unroll
-    for (int j = 0; j < kBins / kTkNT; ++j) hv[sd][j] = gh[sd * kBins + tid + j * kTkNT];
-#pragma unroll
-  for (int j = 0; j < kBins / kTkNT; ++j) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int sd = 0; sd < kShards; ++sd) v += hv[sd][j];
-    h[tid + j * kTkNT] = v;
-  }
+    for (int j = 0; j < kBins / kNT; ++j) hv[sd][j] = gh[sd * kBins + tid + j * kNT];
   const int k = a.k;
-  if (p + 1 <= k) return;                                 // short rows: finalize writes them
-  const int nch = (p + kTkChunk) / kTkChunk;              // chunks covering 0 .. p
-  if (ch >= nch) return;
-  const int n = (int)min((long)kTkChunk, (long)p + 1 - s0);
+  if (p + 1 <= k || ch * kChunk > p) return;             // short rows: finalize writes them
+#pragma unroll
+  for (int j = 0; j < kBins / kNT; ++j) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int sd = 0; sd < kShards; ++sd) x += hv[sd][j];
+    h[tid + j * kNT] = x;
+  }
+  if (tid < kCW) bw[tid] = 0u;
   __syncthreads();
-  find_digit_desc<kTkNT>(h, (uint32_t)k, sh, res);
+  find_digit_desc<kNT>(h, (uint32_t)k, sh, res);
   const uint32_t b1 = res[0];
-  const int nv = min(max(n - tid * kPerThr, 0), kPerThr);          // valid positions of the thread
-  const uint32_t vmask = nv == kPerThr ? 0xFFFFu : ((1u << nv) - 1u);
-  uint32_t gtm = 0, eqm = 0;                              // bit e: position s0 + 16 tid + e
-  uint32_t keys[kPerThr];
+  const int e0 = ch * kChunk + 4 * tid;
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t keys[4];
+  uint32_t gtm = 0, eqm = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThr / 4; ++j) {
-    const float f[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * j + q;
-      keys[e] = order_key(f[q]);
-      const uint32_t d = keys[e] >> 21;
-      gtm |= (uint32_t)(d > b1) << e;
-      eqm |= (uint32_t)(d == b1) << e;
-    }
+  for (int q = 0; q < 4; ++q) {
+    keys[q] = order_key(f[q]);
+    const bool ok = e0 + q <= p;
+    const uint32_t d = keys[q] >> 21;
+    gtm |= (uint32_t)(ok && d > b1) << q;
+    eqm |= (uint32_t)(ok && d == b1) << q;
   }
-  gtm &= vmask;
-  eqm &= vmask;
-  reinterpret_cast<uint16_t*>(a.bits + (long)t * a.bw)[(s0 >> 4) + tid] = (uint16_t)gtm;
+  if (gtm) atomicOr(&bw[tid >> 3], gtm << (4 * (tid & 7)));
   const uint32_t mine = (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16);
-  const uint32_t inc = wave_incl_scan(mine);
-  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-  uint32_t o = (inc - mine) >> 16;                        // candidates of the lanes before
-  uint64_t* slot = a.slots + (((long)t * a.nch + ch) * 4 + wave) * kSlotCap;
-  const uint32_t pos0 = (uint32_t)(s0 + tid * kPerThr);
-  if (eqm) {
+  uint32_t tot;
+  const uint32_t before = block_excl_scan<kNT>(mine, sh, tot);   // also publishes bw
+  uint32_t o = before >> 16;                                      // candidates before this thread
+  uint64_t* slot = a.slots + ((long)t * a.nch + ch) * kCap;
 #pragma unroll
-    for (int e = 0; e < kPerThr; ++e)
-      if ((eqm >> e) & 1u) {
-        if (o < (uint32_t)kSlotCap) slot[o] = ((uint64_t)keys[e] << 32) | (pos0 + e);
-        ++o;
-      }
+  for (int q = 0; q < 4; ++q)
+    if ((eqm >> q) & 1u) {
+      if (o < (uint32_t)kCap) slot[o] = ((uint64_t)keys[q] << 32) | (uint32_t)(e0 + q);
+      ++o;
+    }
+  if (tid < kCW) a.bits[((long)t * a.nch + ch) * kCW + tid] = bw[tid];
+  if (tid == 0) {
+    a.cnt[(long)t * a.nch + ch] = tot;
+    if (ch == 0) { a.bg[2 * t] = b1; a.bg[2 * t + 1] = res[1]; }
   }
-  if (lane == 0) a.cnt[((long)t * a.nch + ch) * 4 + wave] = wtot;
-  if (ch == 0 && tid == 0) a.b1[t] = b1;
 }
 
-// Finalize: one workgroup per row.
-//  * One memory round trip (sized by the batch maxima, so that nothing waits for q_pos) loads
-//    the row's position bitmap (positions above b1), the slot counts and the first entries of
-//    every candidate slot into registers; the candidates' second-digit histogram follows.
-//  * The second radix digit (11 bits) b2 splits the candidates; when few candidates share b2
-//    (the usual case) the exact k-th key K* comes from their pairwise ranks, else from a third
-//    digit (10 bits).  take_eq is how many keys equal to K* to keep.
-//  * Candidates above K* join the bitmap, and so do the keys equal to K*: all of them when they
-//    are exactly take_eq, else the take_eq lowest positions (ranked by a block scan over a tie
-//    bitmap).
-//  * The output is the bitmap's set positions in ascending order (block scan of per-thread
-//    popcounts), staged in LDS and stored coalesced: no sort.
-// Rows with a candidate slot longer than the first trip (crowded digits, massive ties) take
-// their candidates from the row's scores instead.  The row's histogram shards are zeroed for
-// the next call.  Slot indexing uses shifts (no integer division).
-constexpr int kFinNT = 512;
-constexpr int kFinW = kFinNT / 64;                        // waves
-constexpr int kMaxWords = 262144 / 32;                    // bitmap words of the longest row
-constexpr int kWPT = kMaxWords / kFinNT;                  // bitmap words per thread (max)
-constexpr int kSpecPT = 8;                                // first-trip slot loads per thread
-constexpr int kSmall = 64;                                // pairwise ranking of the b2 bin
-
-__global__ void __launch_bounds__(kFinNT) topk_finalize(TkArgs a) {
-  __shared__ uint32_t h2[kBins], h3[kBins];
-  __shared__ uint32_t sh[kFinW];
+// Finalize: one workgroup per chunk again.
+//  * One memory round trip: q_pos, b1 and G (the count above b1), every chunk's counts, the
+//    first entries of every chunk's candidate list (kLoadC per thread), this chunk's bitmap
+//    words and this chunk's scores.
+//  * The second radix digit (11 bits) b2 over the row's candidates, then the third (10 bits)
+//    give the exact k-th key K*; take_eq is how many keys equal to K* to keep (the lowest
+//    positions).  Every workgroup of the row computes the same values.
+//  * The selection before this chunk: the earlier chunks' counts above b1, plus their
+//    candidates above K*, plus the ties at K* they keep.  This chunk's own selection (bitmap
+//    words, its candidates above K*, its kept ties) is written from there in position order.
+// Rows whose candidate lists are longer than the first trip loads (crowded digits, massive
+// ties) take their candidates from the row's scores instead.  Chunk 0 writes short rows and
+// zeroes the row's histogram shards for the next call.
+__global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t sh[kNT / 64];
   __shared__ uint32_t res[2];
-  __shared__ uint32_t scnt[kFinNT];
-  __shared__ uint32_t flags[2];        // [0]: a slot longer than the first trip, [1]: small count
-  __shared__ uint32_t wsum[kFinW];
-  __shared__ uint32_t small[kSmall];
-  __shared__ uint32_t bm[kMaxWords];   // selected positions
-  __shared__ uint32_t tb[kMaxWords];   // ties at K* (rare path)
-  __shared__ int32_t ostage[2048];     // output, staged for coalesced stores
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // ---- one round trip, sized by the batch maxima
-  const int nsub_m = a.nch * 4;                           // <= 256
-  const int wpt_m = (int)((a.bw + kFinNT - 1) / kFinNT);  // <= kWPT
-  int sl = 31 - __clz((kSpecPT * kFinNT) / nsub_m);       // first-trip entries per slot: 2^sl
-  sl = min(sl, 8);                                        // kSlotCap = 256
-  const uint64_t* srow = a.slots + (long)t * nsub_m * kSlotCap;
-  const uint32_t* gbits = a.bits + (long)t * a.bw;
+  __shared__ uint32_t scnt[64];
+  __shared__ uint32_t flag;
+  __shared__ uint32_t bw[kCW];
+  __shared__ uint32_t tw[kCW];
+  __shared__ uint32_t red[4];
+  const int t = blockIdx.y, ch = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch_m = a.nch;
+  const float* row = a.scores + (long)t * a.ld;
+  // ---- one round trip
   const int p = a.q_pos[t];
-  uint32_t wv[kWPT];
+  const float4 v = load4(row, a.ld, ch);
+  const uint32_t b1 = a.bg[2 * t], G = a.bg[2 * t + 1];
+  const uint32_t my_cnt = tid < nch_m ? a.cnt[(long)t * nch_m + tid] : 0u;
+  const uint32_t gw = tid < kCW ? a.bits[((long)t * nch_m + ch) * kCW + tid] : 0u;
+  // first-trip candidate entries: entry f of the row's lists is chunk f >> sl, slot f & (2^sl - 1)
+  int sl = 31 - __clz((kLoadC * kNT) / nch_m);
+  sl = min(sl, 9);                                        // kCap = 512
+  const uint64_t* srow = a.slots + (long)t * nch_m * kCap;
+  uint64_t ev[kLoadC];
 #pragma unroll
-  for (int j = 0; j < kWPT; ++j) {
-    const long w = (long)tid * wpt_m + j;
-    wv[j] = (j < wpt_m && w < a.bw) ? gbits[w] : 0u;
-  }
-  const uint32_t my_cnt = tid < nsub_m ? a.cnt[(long)t * nsub_m + tid] : 0u;
-  uint64_t ev[kSpecPT];
-#pragma unroll
-  for (int u = 0; u < kSpecPT; ++u) {
-    const int f = tid + u * kFinNT;
-    ev[u] = srow[(long)min(f >> sl, nsub_m - 1) * kSlotCap + (f & ((1 << sl) - 1))];
-  }
-  const uint32_t b1 = a.b1[t];
-  {                                                       // nothing below reads the histogram
-    uint32_t* gh = a.hist + (long)t * kShards * kBins;
-    for (int i = tid; i < kShards * kBins; i += kFinNT) gh[i] = 0u;
+  for (int u = 0; u < kLoadC; ++u) {
+    const int f = tid + u * kNT;
+    ev[u] = srow[(long)min(f >> sl, nch_m - 1) * kCap + (f & ((1 << sl) - 1))];
   }
   const int k = a.k;
   int32_t* out = a.idx + (long)t * k;
   if (p + 1 <= k) {                                       // short row: everything, then -1
-    for (int j = tid; j < k; j += kFinNT) out[j] = j <= p ? j : -1;
+    if (ch == 0)
+      for (int j = tid; j < k; j += kNT) out[j] = j <= p ? j : -1;
     return;
   }
-  const int nch = (p + kTkChunk) / kTkChunk;
-  const int nsub = nch * 4;
-  const int nw = (p + 1 + 31) >> 5;                       // bitmap words of this row
-  for (int i = tid; i < kBins; i += kFinNT) { h2[i] = 0u; h3[i] = 0u; }
-#pragma unroll
-  for (int j = 0; j < kWPT; ++j) {
-    const int w = tid * wpt_m + j;
-    if (j < wpt_m) { bm[w] = w < nw ? wv[j] : 0u; tb[w] = 0u; }
+  if (ch * kChunk > p) return;
+  if (ch == 0) {                                          // nothing below reads the histogram
+    uint32_t* gh = a.hist + (long)t * kShards * kBins;
+    for (int i = tid; i < kShards * kBins; i += kNT) gh[i] = 0u;
   }
-  if (tid < 2) flags[tid] = 0u;
-  scnt[tid] = tid < nsub ? my_cnt : 0u;
-  {
-    uint32_t s = wave_incl_scan(tid < nsub ? (my_cnt & 0xFFFFu) : 0u);
-    s = (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
-    if (lane == 0) wsum[wave] = s;
-  }
+  const int nch = p / kChunk + 1;                         // chunks of this row
+  for (int i = tid; i < kBins; i += kNT) h[i] = 0u;
+  if (tid < 64) scnt[tid] = tid < nch ? my_cnt : 0u;
+  if (tid == 0) flag = 0u;
+  if (tid < kCW) { bw[tid] = gw; tw[tid] = 0u; }
+  if (tid < 4) red[tid] = 0u;
   __syncthreads();
-  uint32_t G = 0;                                         // positions above b1 (< k)
-#pragma unroll
-  for (int i = 0; i < kFinW; ++i) G += wsum[i];
-  if (tid < nsub && (my_cnt >> 16) > (1u << sl)) flags[0] = 1u;
-  // this thread's first-trip candidates
+  if (tid < nch && (my_cnt >> 16) > (1u << sl)) flag = 1u;
   uint32_t cvalid = 0;
 #pragma unroll
-  for (int u = 0; u < kSpecPT; ++u) {
-    const int f = tid + u * kFinNT, sidx = f >> sl;       // sidx < kFinNT
-    cvalid |= (uint32_t)(sidx < nsub && (uint32_t)(f & ((1 << sl) - 1)) < (scnt[sidx] >> 16)) << u;
+  for (int u = 0; u < kLoadC; ++u) {
+    const int f = tid + u * kNT, sc = f >> sl;
+    cvalid |= (uint32_t)(sc < nch && (uint32_t)(f & ((1 << sl) - 1)) < (scnt[sc] >> 16)) << u;
   }
-  __syncthreads();                                        // flags
-  const bool streamed = flags[0] != 0u;
+  __syncthreads();                                        // flag
+  const bool streamed = flag != 0u;
   const uint32_t need = (uint32_t)k - G;                  // 1 <= need <= #candidates
-  const float* row = a.scores + (long)t * a.ld;
+  // every candidate of the row: from the first trip, or from the row's scores
   auto each_cand = [&](auto&& fn) {
     if (!streamed) {
 #pragma unroll
-      for (int u = 0; u < kSpecPT; ++u)
+      for (int u = 0; u < kLoadC; ++u)
         if ((cvalid >> u) & 1u) fn((uint32_t)(ev[u] >> 32), (uint32_t)ev[u]);
     } else {
-      for (int s = tid; s <= p; s += kFinNT) {
-        const uint32_t key = order_key(row[s]);
-        if ((key >> 21) == b1) fn(key, (uint32_t)s);
+      for (int c = 0; c < nch; ++c) {
+        const float4 x = load4(row, a.ld, c);
+        const float ff[4] = {x.x, x.y, x.z, x.w};
+        const int e0 = c * kChunk + 4 * tid;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t key = order_key(ff[q]);
+          if (e0 + q <= p && (key >> 21) == b1) fn(key, (uint32_t)(e0 + q));
+        }
       }
     }
   };
-  each_cand([&](uint32_t key, uint32_t) { atomicAdd(&h2[(key >> 10) & 0x7FFu], 1u); });
+  each_cand([&](uint32_t key, uint32_t) { atomicAdd(&h[(key >> 10) & 0x7FFu], 1u); });
   __syncthreads();
-  find_digit_desc<kFinNT>(h2, need, sh, res);
+  find_digit_desc<kNT>(h, need, sh, res);
   const uint32_t b2 = res[0];
-  uint32_t above = res[1];
-  const uint32_t need2 = need - above;                    // >= 1, among the b2 bin
-  const uint32_t c2 = h2[b2];
-  uint32_t kstar, n_eq;
-  if (c2 <= (uint32_t)kSmall) {                           // pairwise ranks within the b2 bin
-    if (tid == 0) flags[1] = 0u;
-    __syncthreads();
-    each_cand([&](uint32_t key, uint32_t) {
-      if (((key >> 10) & 0x7FFu) == b2) small[atomicAdd(&flags[1], 1u)] = key;
-    });
-    __syncthreads();
-    if (tid < (int)c2) {
-      const uint32_t mine = small[tid];
-      uint32_t gt = 0, eq = 0;
-      for (uint32_t j = 0; j < c2; ++j) { const uint32_t x = small[j]; gt += x > mine; eq += x == mine; }
-      if (gt < need2 && need2 <= gt + eq) { res[0] = mine; res[1] = gt; sh[0] = eq; }
-    }
-    __syncthreads();
-    kstar = res[0];
-    above += res[1];
-    n_eq = sh[0];
-    __syncthreads();                                      // sh is reused below
-  } else {                                                // third digit
-    each_cand([&](uint32_t key, uint32_t) {
-      if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h3[key & 0x3FFu], 1u);
-    });
-    __syncthreads();
-    find_digit_desc<kFinNT>(h3, need2, sh, res);
-    kstar = (b1 << 21) | (b2 << 10) | res[0];
-    above += res[1];
-    n_eq = h3[res[0]];
-  }
-  const uint32_t take_eq = need - above;                 // >= 1
-  const bool all_ties = n_eq == take_eq;
-  each_cand([&](uint32_t key, uint32_t pos) {
-    if (key > kstar || (key == kstar && all_ties)) atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-    else if (key == kstar) atomicOr(&tb[pos >> 5], 1u << (pos & 31));
+  const uint32_t need2 = need - res[1];                   // >= 1, among the b2 bin
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kNT) h[i] = 0u;
+  __syncthreads();
+  each_cand([&](uint32_t key, uint32_t) {
+    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h[key & 0x3FFu], 1u);
   });
   __syncthreads();
-  if (!all_ties) {                                        // keep the take_eq lowest tie positions
-    uint32_t nt = 0;
-    for (int j = 0; j < wpt_m; ++j) nt += (uint32_t)__popc(tb[tid * wpt_m + j]);
-    uint32_t tot;
-    uint32_t r = block_excl_scan<kFinNT>(nt, sh, tot);     // ties before this thread's words
-    for (int j = 0; j < wpt_m; ++j) {
-      uint32_t m = tb[tid * wpt_m + j], keep = 0;
-      while (m && r < take_eq) { const uint32_t lb = m & (0u - m); keep |= lb; m ^= lb; ++r; }
-      r += (uint32_t)__popc(m);
-      if (keep) bm[tid * wpt_m + j] |= keep;              // own words only
+  find_digit_desc<kNT>(h, need2, sh, res);
+  const uint32_t kstar = (b1 << 21) | (b2 << 10) | res[0];
+  const uint32_t n_eq = h[res[0]];
+  const uint32_t take_eq = need2 - res[1];                // >= 1
+  const bool all_ties = n_eq == take_eq;
+  // earlier chunks: their candidates above K* and their ties at K*; this chunk's own
+  // candidates above K* (bitmap) and its ties (tie bitmap)
+  const uint32_t c0 = (uint32_t)ch * kChunk, c1 = c0 + kChunk;
+  uint32_t gt_before = 0, eq_before = 0;
+  each_cand([&](uint32_t key, uint32_t pos) {
+    if (pos < c0) {
+      gt_before += key > kstar;
+      eq_before += key == kstar;
+    } else if (pos < c1) {
+      if (key > kstar) atomicOr(&bw[(pos - c0) >> 5], 1u << (pos & 31));
+      else if (key == kstar) atomicOr(&tw[(pos - c0) >> 5], 1u << (pos & 31));
     }
-    __syncthreads();
-  }
-  // ascending output: per-thread popcounts of its contiguous words, one block scan
-  uint32_t nb = 0;
-#pragma unroll
-  for (int j = 0; j < kWPT; ++j) {
-    wv[j] = j < wpt_m ? bm[tid * wpt_m + j] : 0u;
-    nb += (uint32_t)__popc(wv[j]);
-  }
-  uint32_t tot;
-  uint32_t o = block_excl_scan<kFinNT>(nb, sh, tot);
-#pragma unroll
-  for (int j = 0; j < kWPT; ++j) {
-    uint32_t m = wv[j];
-    const int base = (tid * wpt_m + j) * 32;
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      if (o < (uint32_t)k) ostage[o] = base + bit;
-      ++o;
-    }
+  });
+  uint32_t above_b1 = 0;                                  // earlier chunks' counts above b1
+  for (int c = 0; c < ch; ++c) above_b1 += scnt[c] & 0xFFFFu;
+  gt_before += __shfl_xor(gt_before, 1, kWave); gt_before += __shfl_xor(gt_before, 2, kWave);
+  gt_before += __shfl_xor(gt_before, 4, kWave); gt_before += __shfl_xor(gt_before, 8, kWave);
+  gt_before += __shfl_xor(gt_before, 16, kWave); gt_before += __shfl_xor(gt_before, 32, kWave);
+  eq_before += __shfl_xor(eq_before, 1, kWave); eq_before += __shfl_xor(eq_before, 2, kWave);
+  eq_before += __shfl_xor(eq_before, 4, kWave); eq_before += __shfl_xor(eq_before, 8, kWave);
+  eq_before += __shfl_xor(eq_before, 16, kWave); eq_before += __shfl_xor(eq_before, 32, kWave);
+  if ((tid & 63) == 0) {
+    if (gt_before) atomicAdd(&red[0], gt_before);
+    if (eq_before) atomicAdd(&red[1], eq_before);
   }
   __syncthreads();
-  for (int j = tid; j < k; j += kFinNT) out[j] = ostage[j];
+  const uint32_t ties_before = red[1];
+  const uint32_t ties_left = ties_before >= take_eq ? 0u : take_eq - ties_before;   // for this chunk
+  const uint32_t start = above_b1 + red[0] + min(ties_before, take_eq);
+  // this chunk's words: bitmap | kept ties; thread w < kCW owns word w (position order)
+  uint32_t word = 0, tie = 0;
+  if (tid < kCW) { word = bw[tid]; tie = tw[tid]; }
+  uint32_t ntie = (uint32_t)__popc(tie);
+  uint32_t tot;
+  uint32_t r = block_excl_scan<kNT>(ntie, sh, tot);       // ties before this word, in the chunk
+  if (all_ties) {
+    word |= tie;
+  } else {
+    uint32_t m = tie;
+    while (m && r < ties_left) { const uint32_t lb = m & (0u - m); word |= lb; m ^= lb; ++r; }
+  }
+  const uint32_t nb = (uint32_t)__popc(word);
+  __syncthreads();                                        // sh reuse
+  uint32_t o = start + block_excl_scan<kNT>(nb, sh, tot);
+  const int base = (int)c0 + tid * 32;
+  while (word) {
+    const int bit = __ffs(word) - 1;
+    word &= word - 1;
+    if (o < (uint32_t)k) out[o] = base + bit;
+    ++o;
+  }
 }
 
 }  // namespace dsa
@@ -409,19 +358,18 @@ dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn);
 dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn);
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-static int tk_nch(int32_t max_kv_len) { return (max_kv_len + dsa::kTkChunk - 1) / dsa::kTkChunk; }
+static int tk_nch(int32_t max_kv_len) { return (max_kv_len + dsa::kChunk - 1) / dsa::kChunk; }
 
-struct TkLayout { size_t hist, cnt, b1, bits, slots, total; long bw; };
+struct TkLayout { size_t hist, bg, cnt, bits, slots, total; };
 static TkLayout tk_layout(int32_t T, int32_t max_kv_len) {
   TkLayout L{};
   const int nch = tk_nch(max_kv_len);
-  L.bw = (long)nch * (dsa::kTkChunk / 32);                // whole chunks of bits
   L.hist = 0;
-  L.cnt = align256((size_t)T * dsa::kShards * dsa::kBins * 4);
-  L.b1 = L.cnt + align256((size_t)T * nch * 4 * 4);
-  L.bits = L.b1 + align256((size_t)T * 4);
-  L.slots = L.bits + align256((size_t)T * L.bw * 4);
-  L.total = L.slots + align256((size_t)T * nch * 4 * dsa::kSlotCap * 8);
+  L.bg = align256((size_t)T * dsa::kShards * dsa::kBins * 4);
+  L.cnt = L.bg + align256((size_t)T * 2 * 4);
+  L.bits = L.cnt + align256((size_t)T * nch * 4);
+  L.slots = L.bits + align256((size_t)T * nch * dsa::kCW * 4);
+  L.total = L.slots + align256((size_t)T * nch * dsa::kCap * 8);
   return L;
 }
 
@@ -443,20 +391,19 @@ static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t
   if (!scores || !idx) return fail(DSA_ERR_INVALID_ARG, "%s: scores/idx is NULL", fn);
   if (ld < bt->max_kv_len || ld % 4) return fail(DSA_ERR_INVALID_ARG, "%s: ld must be >= max_kv_len and a multiple of 4", fn);
   if ((uintptr_t)scores & 15) return fail(DSA_ERR_INVALID_ARG, "%s: scores must be 16-byte aligned", fn);
-  if (bt->max_kv_len > 64 * dsa::kTkChunk) return fail(DSA_ERR_UNSUPPORTED, "%s: max_kv_len above %d", fn, 64 * dsa::kTkChunk);
+  if (bt->max_kv_len > dsa::kMaxLen) return fail(DSA_ERR_UNSUPPORTED, "%s: max_kv_len above %d", fn, dsa::kMaxLen);
+  if (bt->num_q > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: more than 65535 query tokens", fn);
   const TkLayout L = tk_layout(bt->num_q, bt->max_kv_len);
   if (!ws || ws_bytes < L.total) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, L.total);
   if ((uintptr_t)ws & 255) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
-  if (bt->num_q > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: more than 65535 query tokens", fn);
   dsa::TkArgs a{};
   a.q_pos = bt->q_pos; a.scores = scores; a.ld = ld; a.k = k; a.T = bt->num_q; a.idx = idx;
   a.nch = tk_nch(bt->max_kv_len);
   char* w = (char*)ws;
   a.hist = (uint32_t*)(w + L.hist);
+  a.bg = (uint32_t*)(w + L.bg);
   a.cnt = (uint32_t*)(w + L.cnt);
-  a.b1 = (uint32_t*)(w + L.b1);
   a.bits = (uint32_t*)(w + L.bits);
-  a.bw = L.bw;
   a.slots = (uint64_t*)(w + L.slots);
   *out = a;
   return DSA_OK;
@@ -464,8 +411,9 @@ static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t
 
 // Select + finalize (the row histograms are already in the workspace).
 static void topk_tail(const dsa::TkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(dsa::topk_select, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kTkNT), 0, s, a);
-  hipLaunchKernelGGL(dsa::topk_finalize, dim3((unsigned)a.T), dim3(dsa::kFinNT), 0, s, a);
+  const dim3 grid((unsigned)a.nch, (unsigned)a.T);
+  hipLaunchKernelGGL(dsa::topk_select, grid, dim3(dsa::kNT), 0, s, a);
+  hipLaunchKernelGGL(dsa::topk_finalize, grid, dim3(dsa::kNT), 0, s, a);
 }
 
 extern "C" dsa_status dsa_topk(const dsa_batch* bt, const float* scores, int64_t ld, int32_t k,
@@ -475,7 +423,7 @@ extern "C" dsa_status dsa_topk(const dsa_batch* bt, const float* scores, int64_t
   const dsa_status st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a);
   if (st != DSA_OK || bt->num_q == 0) return st;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(dsa::topk_hist, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kTkNT), 0, s, a);
+  hipLaunchKernelGGL(dsa::topk_hist, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
   topk_tail(a, s);
   return dsa_host::check_launch(fn);
 }

@@ -109,12 +109,12 @@ def test_workspace_sizes():
     assert L.lib.dsa_sparse_attn_workspace_size(8, 128, 2048) > 0
     # a large batch needs no split partials
     assert L.lib.dsa_sparse_attn_workspace_size(4096, 128, 2048) == 0
-    # top-k: at least the per-row histograms; grows with the batch and the row length;
-    # 256-byte multiples
+    # top-k: at least the per-row histograms (4 shards of 2048 bins); grows with the batch and
+    # the row length; 256-byte multiples; nothing for an empty batch
     sz = L.lib.dsa_topk_workspace_size
-    assert sz(8, 65536, 2048) >= 8 * 2048 * 4
+    assert sz(8, 65536, 2048) >= 8 * 4 * 2048 * 4
     assert sz(16, 65536, 2048) > sz(8, 65536, 2048) and sz(8, 131072, 2048) > sz(8, 65536, 2048)
-    assert sz(8, 65536, 2048) % 256 == 0
+    assert sz(3, 65536, 2048) % 256 == 0 and sz(0, 65536, 2048) == 0
 
 
 def test_binding_rejects_cpu_tensors():
