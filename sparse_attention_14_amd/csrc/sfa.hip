@@ -254,14 +254,18 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
                    "{m0}"(ring_base + 3 * kTileB + j * 1024));
     }
   }
-  const int seq = a.q_seq[t];
+  // the selected indices (clamped reads, masked below) and the batch's first cache rows are
+  // issued before the token's sequence id: that id goes to a scalar register, and waiting for
+  // it waits for every load issued before it
   int32_t iv[kMaxKps / 512];
 #pragma unroll
   for (int u = 0; u < kMaxKps / 512; ++u) {
     const int j = tid + 512 * u;
-    iv[u] = j < nkeys ? a.idx[(long)t * a.k + kbeg + j] : 0;
+    iv[u] = a.idx[(long)t * a.k + kbeg + min(j, nkeys - 1)];
   }
   const long kv_lane = a.bt ? 0 : a.kv_start[min(lane, a.B - 1)];
+  asm volatile("" ::: "memory");                       // keep the loads above issued here
+  const int seq = a.q_seq[t];
   const int nkeys_pad = (nkeys + kKT - 1) / kKT * kKT;
   if (a.bt) {
     // Paged cache: the sequence's block table goes through ring slot 2 (free until tile 2 is

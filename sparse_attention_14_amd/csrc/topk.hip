@@ -101,6 +101,11 @@ __device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* s
   __syncthreads();
 }
 
+// Keeps the loads issued above it in place: the compiler would otherwise sink loads that only
+// the non-returning path uses below an early-exit branch, which costs a second memory round
+// trip (the branch waits for q_pos first).  No wait is implied.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
 // This thread's four scores of chunk ch (positions ch * kChunk + 4 tid .. +3); every address
 // lies inside the row's ld columns, positions past p are masked by the caller.
 __device__ __forceinline__ float4 load4(const float* row, long ld, int ch) {
@@ -115,6 +120,7 @@ __global__ void __launch_bounds__(kNT) topk_hist(TkArgs a) {
   const int t = blockIdx.y, ch = blockIdx.x;
   const int p = a.q_pos[t];
   const float4 v = load4(a.scores + (long)t * a.ld, a.ld, ch);
+  issue_fence();
   if (p + 1 <= a.k || ch * kChunk > p) return;
   for (int i = threadIdx.x; i < kBins; i += kNT) h[i] = 0u;
   __syncthreads();
@@ -147,6 +153,7 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
   for (int sd = 0; sd < kShards; ++sd)
 #pragma unroll
     for (int j = 0; j < kBins / kNT; ++j) hv[sd][j] = gh[sd * kBins + tid + j * kNT];
+  issue_fence();
   const int k = a.k;
   if (p + 1 <= k || ch * kChunk > p) return;             // short rows: finalize writes them
 #pragma unroll
@@ -193,8 +200,8 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
 
 // Finalize: one workgroup per chunk again.
 //  * One memory round trip: q_pos, b1 and G (the count above b1), every chunk's counts, the
-//    first entries of every chunk's candidate list (kLoadC per thread), this chunk's bitmap
-//    words and this chunk's scores.
+//    first entries of every chunk's candidate list (kLoadC per thread) and this chunk's bitmap
+//    words.
 //  * The second radix digit (11 bits) b2 over the row's candidates, then the third (10 bits)
 //    give the exact k-th key K*; take_eq is how many keys equal to K* to keep (the lowest
 //    positions).  Every workgroup of the row computes the same values.
@@ -219,10 +226,9 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   const float* row = a.scores + (long)t * a.ld;
   // ---- one round trip
   const int p = a.q_pos[t];
-  const float4 v = load4(row, a.ld, ch);
   const uint32_t b1 = a.bg[2 * t], G = a.bg[2 * t + 1];
-  const uint32_t my_cnt = tid < nch_m ? a.cnt[(long)t * nch_m + tid] : 0u;
-  const uint32_t gw = tid < kCW ? a.bits[((long)t * nch_m + ch) * kCW + tid] : 0u;
+  const uint32_t my_cnt = a.cnt[(long)t * nch_m + min(tid, nch_m - 1)];     // masked below
+  const uint32_t gw = a.bits[((long)t * nch_m + ch) * kCW + min(tid, kCW - 1)];
   // first-trip candidate entries: entry f of the row's lists is chunk f >> sl, slot f & (2^sl - 1)
   int sl = 31 - __clz((kLoadC * kNT) / nch_m);
   sl = min(sl, 9);                                        // kCap = 512
@@ -233,6 +239,7 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
     const int f = tid + u * kNT;
     ev[u] = srow[(long)min(f >> sl, nch_m - 1) * kCap + (f & ((1 << sl) - 1))];
   }
+  issue_fence();
   const int k = a.k;
   int32_t* out = a.idx + (long)t * k;
   if (p + 1 <= k) {                                       // short row: everything, then -1
@@ -247,7 +254,7 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   }
   const int nch = p / kChunk + 1;                         // chunks of this row
   for (int i = tid; i < kBins; i += kNT) h[i] = 0u;
-  if (tid < 64) scnt[tid] = tid < nch ? my_cnt : 0u;
+  if (tid < 64) scnt[tid] = tid < nch ? my_cnt : 0u;     // tid < nch <= nch_m
   if (tid == 0) flag = 0u;
   if (tid < kCW) { bw[tid] = gw; tw[tid] = 0u; }
   if (tid < 4) red[tid] = 0u;
