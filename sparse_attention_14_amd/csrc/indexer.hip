@@ -243,45 +243,95 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   constexpr int NBW = kCK / kBlk / NPH;      // blocks per wave
   float ksr[DOTS ? 1 : NBW];
   if constexpr (!DOTS) {
+    // (flat and paged in separate loops: one uniform branch instead of one per load)
+    if (!a.bt) {
+      const long row0 = kv0 + chunk0;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int r = min((phase + NPH * j) * kBlk + col, last_row);
-      const long row = cache_row(r);
-      ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+      for (int j = 0; j < NBW; ++j) {
+        const long row = row0 + min((phase + NPH * j) * kBlk + col, last_row);
+        ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const long row = cache_row(min((phase + NPH * j) * kBlk + col, last_row));
+        ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+      }
     }
   }
 
+  if constexpr (SEPQ && !DOTS) {
+    // the head weights and key scales land before any direct load is issued: the compiler's
+    // own wait for them would otherwise also wait for every key group, and the groups could
+    // not be consumed as they land
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) retire(wq[mb][i]);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) retire(ksr[j]);
+  }
+
   // ---- DMA: the group's query codes (coalesced, rows of D bytes, swizzled like the key rows)
-  // into the LDS of the last QG key groups, then key group 0.  Q moves on to VGPRs before the
-  // remaining key groups are issued.
+  // into their own LDS region (decode) or the LDS of the last QG key groups (prefill), then the
+  // key groups: all of them (decode), or group 0 with the rest issued once Q sits in VGPRs.
   const unsigned kl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)kl;
   // DMA base (SGPRs): the chunk's first row (flat) or the cache (paged; rows via the table,
   // the host checks that the cache spans < 4 GiB)
   const uint8_t* kchunk = uniform_ptr(a.bt ? a.k_cache : a.k_cache + (kv0 + chunk0) * D);
   auto chunk_off = [&](int rr) -> uint32_t { return (uint32_t)((a.bt ? cache_row(rr) : (long)rr) * D); };
+  // A 1-KiB piece j of Q or of the chunk covers rows j * (1024 / D) + lane * 16 / D; as 1024 / D
+  // is a multiple of the swizzle period, a lane's byte offset within its piece is the same for
+  // every piece.  Whole groups of a flat cache with every row in range (all but the sequence's
+  // last chunk) take that offset as is, with the piece's base in scalar registers; otherwise
+  // rows are clamped (to the group's last token, the chunk's last visible key) or looked up in
+  // the block table per piece.
+  const int lrow = lane * 16 / D;
+  const uint32_t lane_off = (uint32_t)(lrow * D + ((((lane * 16) % D) >> 4) ^ (lrow & (CPR - 1))) * 16);
+  const bool fast_q = (QB >= 1024 && QB % 1024 == 0) && nvalid == G;
+  const bool fast_k = !a.bt && last_row >= kCK - 1;
   {
     const uint8_t* qbase = uniform_ptr(a.q_codes + (long)q_lo * H * D);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    if (fast_q) {
 #pragma unroll
-    for (int it = 0; it < QI; ++it) {
-      const int j = min(wave + NW * it, QJ - 1);
-      const int o = j * 1024 + ln * 16;
-      const int r = o / D;                                 // token * HT + head
-      const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
-      const int tok = min(r / HT, nvalid - 1);
-      dma16(qbase, (uint32_t)((tok * HT + r % HT) * D + c * 16), kl_base + QOFF + j * 1024);
+      for (int it = 0; it < QI; ++it) {
+        const int j = min(wave + NW * it, QJ - 1);
+        dma16(uniform_ptr(qbase + j * 1024), lane_off, kl_base + QOFF + j * 1024);
+      }
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int it = 0; it < QI; ++it) {
+        const int j = min(wave + NW * it, QJ - 1);
+        const int o = j * 1024 + ln * 16;
+        const int r = o / D;                               // token * HT + head
+        const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
+        const int tok = min(r / HT, nvalid - 1);
+        dma16(qbase, (uint32_t)((tok * HT + r % HT) * D + c * 16), kl_base + QOFF + j * 1024);
+      }
     }
   }
+  auto issue_key_pieces = [&](int it0, int it1) {
+    if (fast_k) {
 #pragma unroll
-  for (int it = 0; it < EARLY * PER_GROUP; ++it) {
-    const int j = wave + NW * it;
-    const int o = j * 1024 + lane * 16;
-    const int r = o / D;
-    const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
-    const int rr = min(r, last_row);
-    dma16(kchunk, chunk_off(rr) + (uint32_t)(c * 16), kl_base + j * 1024);
-  }
+      for (int it = it0; it < it1; ++it) {
+        const int j = wave + NW * it;
+        dma16(uniform_ptr(kchunk + j * 1024), lane_off, kl_base + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int it = it0; it < it1; ++it) {
+        const int j = wave + NW * it;
+        const int o = j * 1024 + lane * 16;
+        const int r = o / D;
+        const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
+        const int rr = min(r, last_row);
+        dma16(kchunk, chunk_off(rr) + (uint32_t)(c * 16), kl_base + j * 1024);
+      }
+    }
+  };
+  issue_key_pieces(0, EARLY * PER_GROUP);
   idx_wait_vm<EARLY * PER_GROUP>();                      // Q landed (for this wave)
   idx_lds_barrier();                                     // ... and for every wave
   KFrag<FP8, D> qf[NMB];
@@ -320,15 +370,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     for (int j = 0; j < NBW; ++j) retire(ksr[j]);
   }
   idx_lds_barrier();
-#pragma unroll
-  for (int it = EARLY * PER_GROUP; it < INSTR / NW; ++it) {
-    const int j = wave + NW * it;
-    const int o = j * 1024 + lane * 16;
-    const int r = o / D;
-    const int c = ((o % D) >> 4) ^ (r & (CPR - 1));
-    const int rr = min(r, last_row);
-    dma16(kchunk, chunk_off(rr) + (uint32_t)(c * 16), kl_base + j * 1024);
-  }
+  issue_key_pieces(EARLY * PER_GROUP, INSTR / NW);
 
   // ---- consume the groups as they land
 #pragma unroll
