@@ -189,6 +189,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     const int blk = __shfl(bt_l, (pos >> a.bs_log2) - (chunk0 >> a.bs_log2), kWave);
     return ((long)blk << a.bs_log2) + (pos & ((1 << a.bs_log2) - 1));
   };
+  retire(bt_l);            // landed with the metadata; later lane shuffles of it wait for nothing
   if (q_lo >= q_hi) return;
   if (chunk0 > maxp) return;
   const int t = q_lo + ti;
@@ -210,67 +211,9 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane:
   // rows 8 j + 4 hv + e (e < 4) of the block are four consecutive heads, one 8-byte load of w
   // and one 8- or 16-byte load of q_scale each
+  // Rows past the chunk's last visible key are clamped (never stored).
+  const int last_row = maxp - chunk0;
   float wq[NMB][16];
-  if constexpr (!DOTS) {
-    uint2 wv[NMB][4];
-    uint4 sv[NMB][4];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const long o = (long)tc * H + min(32 * mb + 8 * j + 4 * hv, H - 4);
-        wv[mb][j] = *reinterpret_cast<const uint2*>(a.w + o);
-        if (SF16) { const uint2 x = *reinterpret_cast<const uint2*>((const u16*)a.q_scale + o); sv[mb][j] = uint4{x.x, x.y, 0u, 0u}; }
-        else sv[mb][j] = *reinterpret_cast<const uint4*>((const float*)a.q_scale + o);
-      }
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int h = 32 * mb + 8 * j + 4 * hv + e;
-          const uint32_t ww = e < 2 ? wv[mb][j].x : wv[mb][j].y;
-          const float wf = f16_bits_to_f32((u16)(ww >> (16 * (e & 1))));
-          float qs;
-          if (SF16) { const uint32_t x = e < 2 ? sv[mb][j].x : sv[mb][j].y; qs = f16_bits_to_f32((u16)(x >> (16 * (e & 1)))); }
-          else qs = __uint_as_float(e == 0 ? sv[mb][j].x : e == 1 ? sv[mb][j].y : e == 2 ? sv[mb][j].z : sv[mb][j].w);
-          wq[mb][4 * j + e] = h < H ? wf * qs : 0.f;
-        }
-  }
-  // key scales of this lane's key in each block the wave will visit (row-clamped)
-  const int last_row = maxp - chunk0;        // rows past it are clamped (never stored)
-  constexpr int NBW = kCK / kBlk / NPH;      // blocks per wave
-  float ksr[DOTS ? 1 : NBW];
-  if constexpr (!DOTS) {
-    // (flat and paged in separate loops: one uniform branch instead of one per load)
-    if (!a.bt) {
-      const long row0 = kv0 + chunk0;
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const long row = row0 + min((phase + NPH * j) * kBlk + col, last_row);
-        ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const long row = cache_row(min((phase + NPH * j) * kBlk + col, last_row));
-        ksr[j] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
-      }
-    }
-  }
-
-  if constexpr (SEPQ && !DOTS) {
-    // the head weights and key scales land before any direct load is issued: the compiler's
-    // own wait for them would otherwise also wait for every key group, and the groups could
-    // not be consumed as they land
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) retire(wq[mb][i]);
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) retire(ksr[j]);
-  }
 
   // ---- DMA: the group's query codes (coalesced, rows of D bytes, swizzled like the key rows)
   // into their own LDS region (decode) or the LDS of the last QG key groups (prefill), then the
@@ -283,7 +226,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   // A 1-KiB piece j of Q or of the chunk covers rows j * (1024 / D) + lane * 16 / D; as 1024 / D
   // is a multiple of the swizzle period, a lane's byte offset within its piece is the same for
   // every piece.  Whole groups of a flat cache with every row in range (all but the sequence's
-  // last chunk) take that offset as is, with the piece's base in scalar registers; otherwise
+  // last chunk) take that offset plus the piece's start; otherwise
   // rows are clamped (to the group's last token, the chunk's last visible key) or looked up in
   // the block table per piece.
   const int lrow = lane * 16 / D;
@@ -296,7 +239,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
 #pragma unroll
       for (int it = 0; it < QI; ++it) {
         const int j = min(wave + NW * it, QJ - 1);
-        dma16(uniform_ptr(qbase + j * 1024), lane_off, kl_base + QOFF + j * 1024);
+        dma16(qbase, lane_off + (uint32_t)(j * 1024), kl_base + QOFF + j * 1024);
       }
     } else {
       int ln = lane;
@@ -317,7 +260,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
 #pragma unroll
       for (int it = it0; it < it1; ++it) {
         const int j = wave + NW * it;
-        dma16(uniform_ptr(kchunk + j * 1024), lane_off, kl_base + j * 1024);
+        dma16(kchunk, lane_off + (uint32_t)(j * 1024), kl_base + j * 1024);
       }
     } else {
 #pragma unroll
@@ -332,6 +275,55 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     }
   };
   issue_key_pieces(0, EARLY * PER_GROUP);
+  asm volatile("" ::: "memory");                        // the loads below stay behind the stream
+  // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane: rows
+  // 8 j + 4 hv + e (e < 4) of block mb are heads 32 mb + 8 j + 4 hv + e.  The wave's token rows
+  // of w and q_scale are read through the scalar unit (uniform addresses in the constant
+  // address space): those reads are counted apart from the direct loads of Q and the keys, so
+  // waiting for them never waits for the key stream.  The key scales are applied when the
+  // scores are stored.
+  if constexpr (!DOTS) {
+    typedef const __attribute__((address_space(4))) uint32_t cu32;
+    auto uni = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); };
+    const int tcu = __builtin_amdgcn_readfirstlane(tc);
+    cu32* wrow = (cu32*)(a.w + (long)tcu * H);                                  // f16 pairs
+    cu32* srow = (cu32*)((const char*)a.q_scale + (long)tcu * H * (SF16 ? 2 : 4));
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hb = 32 * mb + 8 * j;                  // heads hb .. hb + 7 (hv picks a half)
+        if (hb >= H) {                                   // uniform: rows past H weigh nothing
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wq[mb][4 * j + e] = 0.f;
+          continue;
+        }
+        // both halves are read (uniform, scalar) and the lane picks one: a per-lane choice of
+        // address would turn these into vector loads
+        const uint32_t w0 = uni(wrow[hb / 2]), w1 = uni(wrow[hb / 2 + 1]);
+        const uint32_t w2 = uni(wrow[hb / 2 + 2]), w3 = uni(wrow[hb / 2 + 3]);
+        const uint32_t wa = hv ? w2 : w0, wb = hv ? w3 : w1;
+        float qs[4];
+        if (SF16) {
+          const uint32_t s0 = uni(srow[hb / 2]), s1 = uni(srow[hb / 2 + 1]);
+          const uint32_t s2 = uni(srow[hb / 2 + 2]), s3 = uni(srow[hb / 2 + 3]);
+          const uint32_t sa = hv ? s2 : s0, sb = hv ? s3 : s1;
+          qs[0] = f16_bits_to_f32((u16)sa); qs[1] = f16_bits_to_f32((u16)(sa >> 16));
+          qs[2] = f16_bits_to_f32((u16)sb); qs[3] = f16_bits_to_f32((u16)(sb >> 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = uni(srow[hb + e]), hi = uni(srow[hb + 4 + e]);
+            qs[e] = __uint_as_float(hv ? hi : lo);
+          }
+        }
+        wq[mb][4 * j + 0] = f16_bits_to_f32((u16)wa) * qs[0];
+        wq[mb][4 * j + 1] = f16_bits_to_f32((u16)(wa >> 16)) * qs[1];
+        wq[mb][4 * j + 2] = f16_bits_to_f32((u16)wb) * qs[2];
+        wq[mb][4 * j + 3] = f16_bits_to_f32((u16)(wb >> 16)) * qs[3];
+      }
+  }
+
   idx_wait_vm<EARLY * PER_GROUP>();                      // Q landed (for this wave)
   idx_lds_barrier();                                     // ... and for every wave
   KFrag<FP8, D> qf[NMB];
@@ -361,14 +353,6 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) retire(qf[mb].v[j]);
-  if constexpr (!DOTS) {
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) retire(wq[mb][i]);
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) retire(ksr[j]);
-  }
   idx_lds_barrier();
   issue_key_pieces(EARLY * PER_GROUP, INSTR / NW);
 
@@ -420,7 +404,6 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
           }
         }
       } else {
-        const float ks = ksr[(kb - phase) / NPH];
         float sum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
@@ -434,20 +417,38 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
           }
         }
         sum += __shfl_xor(sum, 32, kWave);
-        if (hv == 0) scl[ti][r] = sum * ks;
+        if (hv == 0) scl[ti][r] = sum;                   // times the key scale when stored
       }
     }
   }
   if constexpr (!DOTS) {
     __syncthreads();
-    // coalesced score stores: token j of the group, keys chunk0 .. min(chunk0 + kCK, p_j + 1)
+    // key scales of the chunk (one per key, shared by the group's tokens; rows past the last
+    // visible key clamped), then coalesced score stores: token j of the group, keys chunk0 ..
+    // min(chunk0 + kCK, p_j + 1); the stored value also feeds the histogram below
+    constexpr int KPT = kCK / NT;                        // keys per thread
+    float ksv[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int r = min((int)threadIdx.x + i * NT, last_row);
+      const long row = a.bt ? cache_row(r) : kv0 + chunk0 + r;
+      ksv[i] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+    }
     for (int j = 0; j < G; ++j) {
       const int tj = q_lo + j;
       if (tj >= q_hi) break;
       const int pj = a.q_pos[tj];
       const int n = min(kCK, pj + 1 - chunk0);
       float* dst = a.scores + (long)tj * a.ld + chunk0;
-      for (int e = threadIdx.x; e < n; e += NT) dst[e] = scl[j][e];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int e = (int)threadIdx.x + i * NT;
+        if (e < n) {
+          const float v = scl[j][e] * ksv[i];
+          scl[j][e] = v;
+          dst[e] = v;
+        }
+      }
     }
     if (a.hist) {
       // The top-k's first radix pass, fused: histogram of the top 11 key bits of this chunk's
