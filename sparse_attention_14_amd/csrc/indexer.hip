@@ -155,6 +155,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   // Batch metadata.  Small batches (B < 64, T <= 64) load q_start, q_pos and kv_start as
   // lane vectors in one memory round trip and pick entries by lane; larger ones chain loads.
   int q_lo, q_hi, maxp = -1, p;
+  int pg[G];                                 // positions of the group's tokens (-1: none)
   long kv0;
   // Paged caches: the chunk's physical blocks as a lane vector (block j of the chunk in lane
   // j), loaded with the metadata; flat caches: the sequence's first row.
@@ -167,8 +168,10 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     q_lo = __builtin_amdgcn_readlane(qs_l, b) + g * G;
     q_hi = __builtin_amdgcn_readlane(qs_l, b + 1);
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-      if (q_lo + j < q_hi) maxp = max(maxp, __builtin_amdgcn_readlane(qp_l, q_lo + j));
+    for (int j = 0; j < G; ++j) {
+      pg[j] = q_lo + j < q_hi ? __builtin_amdgcn_readlane(qp_l, min(q_lo + j, a.T - 1)) : -1;
+      maxp = max(maxp, pg[j]);
+    }
     const int tt = min(q_lo + ti, a.T - 1);
     p = q_lo + ti < q_hi ? __builtin_amdgcn_readlane(qp_l, tt) : -1;
     kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_l >> 32), b) << 32) |
@@ -177,8 +180,10 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     q_lo = a.q_start[b] + g * G;
     q_hi = a.q_start[b + 1];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-      if (q_lo + j < q_hi) maxp = max(maxp, a.q_pos[q_lo + j]);
+    for (int j = 0; j < G; ++j) {
+      pg[j] = q_lo + j < q_hi ? a.q_pos[q_lo + j] : -1;
+      maxp = max(maxp, pg[j]);
+    }
     p = q_lo + ti < q_hi ? a.q_pos[q_lo + ti] : -1;
     kv0 = a.bt ? 0 : a.kv_start[b];
   }
@@ -214,6 +219,20 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   // Rows past the chunk's last visible key are clamped (never stored).
   const int last_row = maxp - chunk0;
   float wq[NMB][16];
+
+  // Key scales of the chunk for the score stores (one per key, shared by the group's tokens;
+  // rows past the last visible key clamped).  Issued ahead of the direct loads, they land with
+  // the first key group and their first use (the stores) comes after the last one.
+  constexpr int KPT = kCK / NT;                          // keys per thread
+  uint32_t ksraw[DOTS ? 1 : KPT];
+  if constexpr (!DOTS) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int r = min((int)threadIdx.x + i * NT, last_row);
+      const long row = a.bt ? cache_row(r) : kv0 + chunk0 + r;
+      ksraw[i] = SF16 ? (uint32_t)((const u16*)a.k_scale)[row] : ((const uint32_t*)a.k_scale)[row];
+    }
+  }
 
   // ---- DMA: the group's query codes (coalesced, rows of D bytes, swizzled like the key rows)
   // into their own LDS region (decode) or the LDS of the last QG key groups (prefill), then the
@@ -423,28 +442,19 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   }
   if constexpr (!DOTS) {
     __syncthreads();
-    // key scales of the chunk (one per key, shared by the group's tokens; rows past the last
-    // visible key clamped), then coalesced score stores: token j of the group, keys chunk0 ..
+    // coalesced score stores, times the key scales: token j of the group, keys chunk0 ..
     // min(chunk0 + kCK, p_j + 1); the stored value also feeds the histogram below
-    constexpr int KPT = kCK / NT;                        // keys per thread
-    float ksv[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int r = min((int)threadIdx.x + i * NT, last_row);
-      const long row = a.bt ? cache_row(r) : kv0 + chunk0 + r;
-      ksv[i] = SF16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
-    }
     for (int j = 0; j < G; ++j) {
       const int tj = q_lo + j;
       if (tj >= q_hi) break;
-      const int pj = a.q_pos[tj];
-      const int n = min(kCK, pj + 1 - chunk0);
+      const int n = min(kCK, pg[j] + 1 - chunk0);
       float* dst = a.scores + (long)tj * a.ld + chunk0;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int e = (int)threadIdx.x + i * NT;
         if (e < n) {
-          const float v = scl[j][e] * ksv[i];
+          const float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
+          const float v = scl[j][e] * ks;
           scl[j][e] = v;
           dst[e] = v;
         }
@@ -461,9 +471,8 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
       for (int j = 0; j < G; ++j) {
         const int tj = q_lo + j;
         if (tj >= q_hi) break;
-        const int pj = a.q_pos[tj];
-        if (pj + 1 <= a.hist_k) continue;
-        const int n = min(kCK, pj + 1 - chunk0);
+        if (pg[j] + 1 <= a.hist_k) continue;
+        const int n = min(kCK, pg[j] + 1 - chunk0);
         for (int e = threadIdx.x; e < n; e += NT) atomicAdd(&hl[j * kHistBins + (order_key(scl[j][e]) >> 21)], 1u);
       }
       __syncthreads();
