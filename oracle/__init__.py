@@ -29,7 +29,9 @@ from .topk import topk_select
 from .sfa import sparse_attention
 from .step import decode_step
 from .paged import paged_rows, flatten_paged
+from .projections import w8a8_dequant, linear, layer_norm, indexer_projections
 
 __all__ = ["bf16_encode", "bf16_decode", "e4m3_encode", "e4m3_decode", "fp16_round",
            "hadamard", "apply_rope", "quantize_rows", "prolog_rows", "indexer_prolog",
-           "indexer_dots", "indexer_scores", "topk_select", "sparse_attention", "decode_step"]
+           "indexer_dots", "indexer_scores", "topk_select", "sparse_attention", "decode_step",
+           "w8a8_dequant", "linear", "layer_norm", "indexer_projections"]
