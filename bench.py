@@ -307,6 +307,8 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(sets[0].buf.out, ref)
 
+    proj = projections_stage(stream, dev)
+
     idx_tops = idx_ops / (stage_us["indexer"] * 1e-6) / 1e12
     sfa_gbps = n_sel * 1152 / (stage_us["sfa"] * 1e-6) / 1e9
     # roofline of the dominant kernel: among the single-kernel calls, the longest per launch;
@@ -346,11 +348,68 @@ def main():
                      "traffic": recorded_traffic(kernel_name), "bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(stage_us[dominant], 3)},
         "wall_s_timed": round(wall, 4),
+        "projections": proj,
     }
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def projections_stage(stream, dev) -> dict:
+    """The Indexer Prolog's upstream linears at the pages' decode shape (8 tokens; W8A8
+    1536 -> 64 x 128, key and weight linears from a 7168-wide hidden state), timed alone on
+    rotating weight copies (past the MALL); HBM-bound on the weights."""
+    import torch
+    from sparse_attention_14_amd import dsa
+    T, R, H, D, hidden = 8, 1536, 64, 128, 7168
+    g = torch.Generator(device=dev).manual_seed(77)
+    wbytes = H * D * R + H * D * 2 + (D + H) * hidden * 2
+    n_sets = min(32, max(4, int(np.ceil(4 * MALL_BYTES / wbytes))))
+    rint = lambda shape: torch.randint(-127, 128, shape, generator=g, device=dev, dtype=torch.int8)
+    rn = lambda *shape: torch.randn(*shape, generator=g, device=dev)
+    qa = rint((T, R))
+    qa_s = (torch.rand(T, generator=g, device=dev) * 0.02 + 1e-3).half()
+    x = rn(T, hidden).bfloat16()
+    gam, bet = rn(D), rn(D)
+    sets = [(rint((H * D, R)), (torch.rand(H * D, generator=g, device=dev) * 0.002 + 1e-4).half(),
+             (rn(D, hidden) / hidden ** 0.5).bfloat16(), (rn(H, hidden) / hidden ** 0.5).bfloat16())
+            for _ in range(n_sets)]
+    q_pre = torch.empty((T, H * D), dtype=torch.float32, device=dev)
+    k_pre = torch.empty((T, D), dtype=torch.float32, device=dev)
+    wt = torch.empty((T, H), dtype=torch.float16, device=dev)
+    ws = torch.empty(int(dsa.lib.dsa_indexer_projections_workspace_size(T, H, D)), dtype=torch.uint8,
+                     device=dev)
+
+    def run(sw):
+        dsa.dsa_indexer_projections(qa, qa_s, sw[0], sw[1], x, sw[2], gam, bet, 1e-6, sw[3],
+                                    H ** -0.5, q_pre=q_pre, k_pre=k_pre, weight=wt, ws=ws)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        run(sets[0])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        for sw in sets:
+            run(sw)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(2, 64 // n_sets)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / (reps * n_sets)
+    alg = wbytes + T * (R + hidden * 2) + T * (H * D + D) * 4 + T * H * 2
+    return {"shape": {"tokens": T, "q_rank": R, "heads": H, "head_dim": D, "hidden": hidden},
+            "us": round(us, 3), "algorithmic_bytes": alg,
+            "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "rotating_weight_sets": n_sets}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:

@@ -146,6 +146,47 @@ dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
                                 const int8_t* q_codes, const int8_t* k_cache,
                                 int32_t* dots, int64_t ld, void* stream);
 
+/* ---------------------------------------------------------------- upstream projections ---- */
+/*
+ * [PRO] Indexer Prolog formulas, the parts before RoPE: the indexer query's W8A8 linear
+ * q_pre = DeQuant(q_a . w_qb) (q_a and w_qb int8, dequant factors FP16 per token and per output
+ * channel: ((float)acc * q_a_scale[t]) * w_qb_scale[n], the int32 contraction exact, as in the
+ * [AQ] page's Int8 GEMM), the indexer key's k_pre = LayerNorm(x . w_k) (over the D key values,
+ * population variance, gamma, beta and eps given), and the head weights
+ * weight = (x . w_proj) * weight_scale rounded to FP16.  q_pre and k_pre are fp32 and feed
+ * dsa_indexer_prolog as its q_in ([T, H, D]) and k_in ([T, D]).
+ * Decode shapes only: 1 <= num_q <= 8, H + D <= 256, q_rank a multiple of 256 with
+ * num_q * q_rank <= 65536, hidden a multiple of 512 with num_q * hidden <= 131072.
+ * Weights are stored as rows of their input dimension: w_qb [H*D, q_rank] int8, w_k [D, hidden]
+ * and w_proj [H, hidden] bf16 (16-byte aligned).  The bf16 sums are fp32 in a fixed order.
+ */
+typedef struct dsa_projections {
+  int32_t num_q;            /* T                                                          */
+  int32_t q_rank;           /* contraction length of the query linear (e.g. 1536)         */
+  int32_t hidden;           /* contraction length of the key and weight linears (7168)    */
+  int32_t H, D;             /* indexer heads, head dim                                    */
+  const int8_t* q_a;        /* device [T, q_rank] int8                                    */
+  const void* q_a_scale;    /* device [T] fp16                                            */
+  const int8_t* w_qb;       /* device [H*D, q_rank] int8                                  */
+  const void* w_qb_scale;   /* device [H*D] fp16                                          */
+  const void* x;            /* device [T, hidden] bf16                                    */
+  const void* w_k;          /* device [D, hidden] bf16                                    */
+  const float* ln_gamma;    /* device [D] fp32                                            */
+  const float* ln_beta;     /* device [D] fp32                                            */
+  float ln_eps;             /* >= 0                                                       */
+  const void* w_proj;       /* device [H, hidden] bf16                                    */
+  float weight_scale;
+  float* q_pre;             /* device out [T, H*D] fp32                                   */
+  float* k_pre;             /* device out [T, D] fp32                                     */
+  void* weight;             /* device out [T, H] fp16                                     */
+} dsa_projections;
+
+/* Workspace bytes for dsa_indexer_projections (slice partial sums; no zero-fill needed). */
+size_t dsa_indexer_projections_workspace_size(int32_t num_q, int32_t H, int32_t D);
+/* Outside the decode shapes: DSA_ERR_UNSUPPORTED.  ws: device, 16-byte aligned. */
+dsa_status dsa_indexer_projections(const dsa_projections* args, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* ---------------------------------------------------------------- top-k ------------------- */
 /*
  * [LI] TopK; [SFA] step 2 index convention.  For every token t: the k_eff = min(k, p_t + 1)

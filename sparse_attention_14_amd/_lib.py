@@ -47,6 +47,16 @@ _BP = ctypes.POINTER(DsaBatch)
 _PP = ctypes.POINTER(DsaPaging)
 
 # name -> (restype, argtypes); mirrors include/dsa.h
+class DsaProjections(ctypes.Structure):
+    _fields_ = [("num_q", ctypes.c_int32), ("q_rank", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("q_a", ctypes.c_void_p), ("q_a_scale", ctypes.c_void_p), ("w_qb", ctypes.c_void_p),
+                ("w_qb_scale", ctypes.c_void_p), ("x", ctypes.c_void_p), ("w_k", ctypes.c_void_p),
+                ("ln_gamma", ctypes.c_void_p), ("ln_beta", ctypes.c_void_p), ("ln_eps", ctypes.c_float),
+                ("w_proj", ctypes.c_void_p), ("weight_scale", ctypes.c_float),
+                ("q_pre", ctypes.c_void_p), ("k_pre", ctypes.c_void_p), ("weight", ctypes.c_void_p)]
+
+
 SIGNATURES = {
     "dsa_indexer_prolog": (ctypes.c_int, [ctypes.POINTER(DsaPrologCfg), _I32, _P, _P, _P, _P, _P,
                                           _I32, _P, _P, _P, _P, _P, _P, _P]),
@@ -69,6 +79,8 @@ SIGNATURES = {
                                               _P, _P, _P, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "dsa_sparse_attn_decode_paged": (ctypes.c_int, [_BP, _PP, _I32, _P, _P, _I64, _P, _I32, _P,
                                                     ctypes.c_float, _P, _P, _SZ, _P]),
+    "dsa_indexer_projections_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "dsa_indexer_projections": (ctypes.c_int, [ctypes.POINTER(DsaProjections), _P, _SZ, _P]),
     "dsa_last_error": (ctypes.c_char_p, []),
     "dsa_version": (ctypes.c_char_p, []),
 }

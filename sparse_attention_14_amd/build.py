@@ -23,7 +23,7 @@ CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno
           # packed fp32 VALU ops stay off: scalar and float2 code compile to unpacked ops
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
-SOURCES = ["api.hip", "prolog.hip", "indexer.hip", "topk.hip", "sfa.hip"]
+SOURCES = ["api.hip", "prolog.hip", "proj.hip", "indexer.hip", "topk.hip", "sfa.hip"]
 # per-source flags: the indexer's MFMA accumulators are consumed by VALU right away, so they
 # are kept in VGPRs (no accumulator-register copies in the epilogue)
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 from ._lib import (DSA_BF16, DSA_F16, DSA_F32, DSA_FP8_E4M3, DSA_I8, DsaBatch, DsaPaging, DsaPrologCfg,
-                   check, lib)
+                   DsaProjections, check, lib)
 
 D_QK, D_V = 576, 512
 
@@ -371,6 +371,48 @@ def dsa_sparse_attn_decode_paged(batch: Batch, paging: Paging, q: torch.Tensor, 
         _ptr(sink), ctypes.c_float(scale), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream()))
     return out
+
+
+def dsa_indexer_projections(q_a, q_a_scale, w_qb, w_qb_scale, x, w_k, ln_gamma, ln_beta,
+                            ln_eps: float, w_proj, weight_scale: float, q_pre=None, k_pre=None,
+                            weight=None, ws=None):
+    """The Indexer Prolog's upstream projections -> (q_pre fp32 [T, H*D], k_pre fp32 [T, D],
+    weight fp16 [T, H]).  q_a int8 [T, R], q_a_scale fp16 [T], w_qb int8 [H*D, R],
+    w_qb_scale fp16 [H*D], x bf16 [T, hidden], w_k bf16 [D, hidden], ln_gamma/ln_beta fp32 [D],
+    w_proj bf16 [H, hidden]."""
+    T, R = q_a.shape
+    D, hidden = w_k.shape
+    H = w_proj.shape[0]
+    _need(q_a, "q_a", torch.int8, (T, R))
+    _need(q_a_scale, "q_a_scale", torch.float16, (T,))
+    _need(w_qb, "w_qb", torch.int8, (H * D, R))
+    _need(w_qb_scale, "w_qb_scale", torch.float16, (H * D,))
+    _need(x, "x", torch.bfloat16, (T, hidden))
+    _need(w_k, "w_k", torch.bfloat16, (D, hidden))
+    _need(ln_gamma, "ln_gamma", torch.float32, (D,))
+    _need(ln_beta, "ln_beta", torch.float32, (D,))
+    _need(w_proj, "w_proj", torch.bfloat16, (H, hidden))
+    dev = q_a.device
+    if q_pre is None:
+        q_pre = torch.empty((T, H * D), dtype=torch.float32, device=dev)
+    if k_pre is None:
+        k_pre = torch.empty((T, D), dtype=torch.float32, device=dev)
+    if weight is None:
+        weight = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _need(q_pre, "q_pre", torch.float32, (T, H * D))
+    _need(k_pre, "k_pre", torch.float32, (T, D))
+    _need(weight, "weight", torch.float16, (T, H))
+    if ws is None:
+        ws = torch.empty(max(int(lib.dsa_indexer_projections_workspace_size(T, H, D)), 1),
+                         dtype=torch.uint8, device=dev)
+    _need(ws, "ws", torch.uint8)
+    args = DsaProjections(T, R, hidden, H, D, q_a.data_ptr(), q_a_scale.data_ptr(), w_qb.data_ptr(),
+                          w_qb_scale.data_ptr(), x.data_ptr(), w_k.data_ptr(), ln_gamma.data_ptr(),
+                          ln_beta.data_ptr(), ln_eps, w_proj.data_ptr(), weight_scale,
+                          q_pre.data_ptr(), k_pre.data_ptr(), weight.data_ptr())
+    check("dsa_indexer_projections", lib.dsa_indexer_projections(ctypes.byref(args), _ptr(ws),
+                                                                 ws.numel(), _stream()))
+    return q_pre, k_pre, weight
 
 
 def dsa_last_error() -> str:

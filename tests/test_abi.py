@@ -159,3 +159,23 @@ def test_paged_validation_before_any_device_call():
     pg = PP()
     assert lib.dsa_indexer_topk_paged(ctypes.byref(e), ctypes.byref(pg), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, 2048, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_sparse_attn_decode_paged(ctypes.byref(e), ctypes.byref(pg), 128, None, None, 576, None, 2048, None, ctypes.c_float(0.04), None, None, 0, None) == L.DSA_OK
+
+
+def test_projections_validation_before_any_device_call():
+    L = _lib()
+    lib = L.lib
+    P = 0x1000
+    def args(T=8, R=1536, hidden=7168, H=64, D=128, null=False):
+        return L.DsaProjections(T, R, hidden, H, D, P, P, P, P, P, P, None if null else P, P, 1e-6,
+                                P, 0.125, P, P, P)
+    big = 1 << 30
+    assert lib.dsa_indexer_projections(None, ctypes.c_void_p(P), big, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_projections(ctypes.byref(args(T=9)), ctypes.c_void_p(P), big, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_projections(ctypes.byref(args(R=1000)), ctypes.c_void_p(P), big, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_projections(ctypes.byref(args(hidden=7000)), ctypes.c_void_p(P), big, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_projections(ctypes.byref(args(H=200)), ctypes.c_void_p(P), big, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_indexer_projections(ctypes.byref(args(null=True)), ctypes.c_void_p(P), big, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_projections(ctypes.byref(args()), ctypes.c_void_p(P), 16, None) == L.DSA_ERR_WORKSPACE
+    assert lib.dsa_indexer_projections(ctypes.byref(args(T=0)), None, 0, None) == L.DSA_OK
+    assert lib.dsa_indexer_projections_workspace_size(8, 64, 128) >= 8 * 8 * 192 * 4
+    assert lib.dsa_indexer_projections_workspace_size(0, 64, 128) == 0
