@@ -10,16 +10,19 @@
 // At decode the token count T is tiny (8 at batch 4 with MTP1) and every linear is a stream over
 // its weight matrix (w_qb: 8192 x 1536 int8 = 12 MiB; w_k and w_proj: 192 x 7168 bf16 = 2.6 MiB),
 // so the kernels are built to spread the weight rows over every CU, not around a matrix core:
-//   proj_w8a8     workgroup = 16 output channels; lane (channel c = lane / 16, part kp = lane % 16)
+//   w8a8 part     workgroup = 16 output channels; lane (channel c = lane / 16, part kp = lane % 16)
 //                 reads one sixteenth of the channel's int8 row in 16-byte pieces and contracts it
 //                 with the T activation rows (LDS) on v_dot4_i32_i8, exact int32; four xor
 //                 shuffles sum the parts; dequant (acc * a_scale) * b_scale in fp32
-//   proj_bf16     the key and weight linears as one: workgroup = (32 output rows, one of S = 16
+//   bf16 part     the key and weight linears as one: workgroup = (32 output rows, one of S = 16
 //                 (or 8) slices of the hidden dim); same lane split, fp32 FMAs on bf16 widened
 //                 exactly; the S slice sums go to a workspace (a fixed summation order:
 //                 deterministic)
+// Both parts run in one launch (proj_linears), the w8a8 workgroups first.
 //   proj_finish   workgroup per token: sums the slices in order, LayerNorm over the D key values
 //                 (fp32, two-pass mean / variance), and the weights times the scale, to FP16.
+#include <algorithm>
+
 #include "common.h"
 
 namespace dsa {
@@ -39,11 +42,10 @@ struct PjArgs {
 // 16 output channels per workgroup (4 per wave), each row split in 16 parts: 512 workgroups
 // for the 8192 channels of the pages' shape, so every CU streams a small share of w_qb.
 constexpr int kQCols = 16;
-__global__ void __launch_bounds__(256) proj_w8a8(PjArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char qa_l[];   // [T][R] int8
+__device__ __forceinline__ void w8a8_block(const PjArgs& a, int blk, unsigned char* qa_l) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 4, kp = lane & 15;
-  const int n = blockIdx.x * kQCols + wave * 4 + c;
+  const int n = blk * kQCols + wave * 4 + c;
   const int nc = min(n, a.N - 1);                                      // clamped row (no store)
   const int seg = a.R / 16;                                            // bytes per part (16k)
   const int8_t* brow = a.wqb + (long)nc * a.R + kp * seg;
@@ -83,15 +85,14 @@ __global__ void __launch_bounds__(256) proj_w8a8(PjArgs a) {
       a.q_pre[(long)t * a.N + n] = ((float)acc[t] * f16_bits_to_f32(a.qa_scale[t])) * sb;
 }
 
-// Output row n of the stacked [w_k; w_proj] (D + H rows), hidden slice blockIdx.y.
-__global__ void __launch_bounds__(256) proj_bf16(PjArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float x_l[];          // [T][slice] fp32
+// Output row n of the stacked [w_k; w_proj] (D + H rows), hidden slice `sl`.
+__device__ __forceinline__ void bf16_block(const PjArgs& a, int blk, int sl, float* x_l) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 3, kp = lane & 7;
   const int NT = a.D + a.H;
-  const int n = blockIdx.x * kPjCols + wave * 8 + c;
+  const int n = blk * kPjCols + wave * 8 + c;
   const int nc = min(n, NT - 1);
-  const int slice = a.hidden / a.S, k0 = blockIdx.y * slice;
+  const int slice = a.hidden / a.S, k0 = sl * slice;
   const int seg = slice / 8;                                           // elements per part (8k)
   const u16* wrow = (nc < a.D ? a.wk + (long)nc * a.hidden : a.wp + (long)(nc - a.D) * a.hidden) + k0 + kp * seg;
   for (int i = tid * 8; i < a.T * slice; i += 256 * 8) {               // 8 activations per load
@@ -139,16 +140,30 @@ __global__ void __launch_bounds__(256) proj_bf16(PjArgs a) {
   if (n >= NT) return;
 #pragma unroll
   for (int t = 0; t < kPjMaxT; ++t)
-    if (t == kp && t < a.T) a.part[((long)blockIdx.y * a.T + t) * NT + n] = acc[t];
+    if (t == kp && t < a.T) a.part[((long)sl * a.T + t) * NT + n] = acc[t];
+}
+
+// The query's W8A8 linear and the key/weight linears are independent: one launch runs both, the
+// first nq workgroups on w_qb, the rest on the bf16 weights (so the two streams overlap).
+__global__ void __launch_bounds__(256) proj_linears(PjArgs a, int nq, int ncb) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char pj_lds[];
+  const int b = blockIdx.x;
+  if (b < nq) w8a8_block(a, b, pj_lds);
+  else bf16_block(a, (b - nq) % ncb, (b - nq) / ncb, reinterpret_cast<float*>(pj_lds));
 }
 
 __global__ void __launch_bounds__(256) proj_finish(PjArgs a) {
   __shared__ float red[2][4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NT = a.D + a.H;
+  // every slice's partial is loaded before the first add (one round trip), then summed in order
+  float pv[kPjSlices];
+  const int nn = min(tid, NT - 1);
+#pragma unroll
+  for (int s = 0; s < kPjSlices; ++s) pv[s] = a.part[((long)min(s, a.S - 1) * a.T + t) * NT + nn];
   float v = 0.f;
-  if (tid < NT)
-    for (int s = 0; s < a.S; ++s) v += a.part[((long)s * a.T + t) * NT + tid];
+#pragma unroll
+  for (int s = 0; s < kPjSlices; ++s) v += s < a.S ? pv[s] : 0.f;
   const bool key = tid < a.D;
   // LayerNorm over the key values (threads 0 .. D-1): two block sums
   auto block_sum = [&](float x, int slot) {
@@ -213,10 +228,10 @@ extern "C" dsa_status dsa_indexer_projections(const dsa_projections* p, void* ws
   a.gamma = p->ln_gamma; a.beta = p->ln_beta; a.eps = p->ln_eps; a.wscale = p->weight_scale;
   a.q_pre = p->q_pre; a.k_pre = p->k_pre; a.weight = (dsa::u16*)p->weight; a.part = (float*)ws;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(dsa::proj_w8a8, dim3((unsigned)((a.N + dsa::kQCols - 1) / dsa::kQCols)), dim3(256),
-                     (unsigned)(T * a.R), s, a);
-  hipLaunchKernelGGL(dsa::proj_bf16, dim3((unsigned)((a.D + a.H + dsa::kPjCols - 1) / dsa::kPjCols), (unsigned)a.S),
-                     dim3(256), (unsigned)(T * (a.hidden / a.S) * 4), s, a);
+  const int nq = (a.N + dsa::kQCols - 1) / dsa::kQCols;
+  const int ncb = (a.D + a.H + dsa::kPjCols - 1) / dsa::kPjCols;
+  const unsigned lds = (unsigned)std::max(T * a.R, T * (a.hidden / a.S) * 4);
+  hipLaunchKernelGGL(dsa::proj_linears, dim3((unsigned)(nq + ncb * a.S)), dim3(256), lds, s, a, nq, ncb);
   hipLaunchKernelGGL(dsa::proj_finish, dim3((unsigned)T), dim3(256), 0, s, a);
   return dsa_host::check_launch(fn);
 }
