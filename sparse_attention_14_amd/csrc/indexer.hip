@@ -207,18 +207,16 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   const int nvalid = min(G, q_hi - q_lo);                // query tokens of this group
   constexpr int QI = (QB + NW * 1024 - 1) / (NW * 1024); // Q loads per wave (1 KiB each)
   constexpr int QJ = QB >= 1024 ? QB / 1024 : 1;         // Q loads in all
-  // key group 0 travels with Q; groups 1.. are issued once Q sits in VGPRs (the last QG of
-  // them overwrite Q's LDS) and land while the earlier groups are being consumed
+  // decode: every key group travels with Q; prefill: key group 0 travels with Q and groups
+  // 1.. are issued once Q sits in VGPRs (the last QG of them overwrite Q's LDS); either way the
+  // groups are consumed as they land
   constexpr int EARLY = SEPQ ? kGroups : 1;
   constexpr unsigned QOFF = SEPQ ? KB : (kGroups - QG) * GB;   // Q's LDS offset
   static_assert(SEPQ || EARLY + QG <= kGroups, "Q staging overlaps the first key group");
   static_assert(QB <= QG * GB && QB % 1024 == 0 || QB < 1024, "Q staging does not fit");
-  // (w * q_scale) for the 16 accumulator rows of each M-block held by this lane:
-  // rows 8 j + 4 hv + e (e < 4) of the block are four consecutive heads, one 8-byte load of w
-  // and one 8- or 16-byte load of q_scale each
   // Rows past the chunk's last visible key are clamped (never stored).
   const int last_row = maxp - chunk0;
-  float wq[NMB][16];
+  float wq[NMB][16];                                     // set once the key stream is issued
 
   // Key scales of the chunk for the score stores (one per key, shared by the group's tokens;
   // rows past the last visible key clamped).  Issued ahead of the direct loads, they land with
