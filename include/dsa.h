@@ -197,8 +197,11 @@ dsa_status dsa_indexer_projections(const dsa_projections* args, void* ws, size_t
  *   scores device [T, ld] fp32 (as written by dsa_indexer_scores), idx device [T, k] int32.
  *   ws: device workspace of at least dsa_topk_workspace_size(T, max_kv_len, k) bytes,
  *       256-byte aligned, ZERO-FILLED before its first use; every call leaves the part that
- *       must start at zero (the per-row histograms) zeroed again, so a workspace is allocated
- *       and cleared once and then reused.  Calls sharing a workspace must not overlap.
+ *       must start at zero (the per-row histograms, at the start of the buffer) zeroed again,
+ *       so a workspace is allocated and cleared once and then reused.  A workspace shared by
+ *       calls of different shapes must be sized with the largest num_q and the largest
+ *       max_kv_len among them (the other regions sit at the end of the buffer, past every
+ *       call's histograms).  Calls sharing a workspace must not overlap.
  *       max_kv_len <= 262144.
  */
 size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k);

@@ -367,23 +367,28 @@ dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn);
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static int tk_nch(int32_t max_kv_len) { return (max_kv_len + dsa::kChunk - 1) / dsa::kChunk; }
 
-struct TkLayout { size_t hist, bg, cnt, bits, slots, total; };
+// Workspace: the row histograms at the start (the only part that must stay zero between
+// calls), the other regions (written before they are read) packed against the end of the
+// caller's buffer.  A buffer sized for the largest num_q and max_kv_len of a series of calls
+// then never lets one call's lists land on another call's histogram rows.
+struct TkLayout { size_t hist, bg, cnt, bits, slots, others; };
 static TkLayout tk_layout(int32_t T, int32_t max_kv_len) {
   TkLayout L{};
   const int nch = tk_nch(max_kv_len);
-  L.hist = 0;
-  L.bg = align256((size_t)T * dsa::kShards * dsa::kBins * 4);
+  L.hist = align256((size_t)T * dsa::kShards * dsa::kBins * 4);
+  L.bg = 0;                                              // offsets within the other regions
   L.cnt = L.bg + align256((size_t)T * 2 * 4);
   L.bits = L.cnt + align256((size_t)T * nch * 4);
   L.slots = L.bits + align256((size_t)T * nch * dsa::kCW * 4);
-  L.total = L.slots + align256((size_t)T * nch * dsa::kCap * 8);
+  L.others = L.slots + align256((size_t)T * nch * dsa::kCap * 8);
   return L;
 }
 
 extern "C" size_t dsa_topk_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k) {
   (void)k;
   if (num_q <= 0 || max_kv_len <= 0) return 0;
-  return tk_layout(num_q, max_kv_len).total;
+  const TkLayout L = tk_layout(num_q, max_kv_len);
+  return L.hist + L.others;
 }
 
 // Validates a top-k call and fills the kernel arguments (no launch).
@@ -401,17 +406,18 @@ static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t
   if (bt->max_kv_len > dsa::kMaxLen) return fail(DSA_ERR_UNSUPPORTED, "%s: max_kv_len above %d", fn, dsa::kMaxLen);
   if (bt->num_q > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: more than 65535 query tokens", fn);
   const TkLayout L = tk_layout(bt->num_q, bt->max_kv_len);
-  if (!ws || ws_bytes < L.total) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, L.total);
+  if (!ws || ws_bytes < L.hist + L.others) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, L.hist + L.others);
   if ((uintptr_t)ws & 255) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   dsa::TkArgs a{};
   a.q_pos = bt->q_pos; a.scores = scores; a.ld = ld; a.k = k; a.T = bt->num_q; a.idx = idx;
   a.nch = tk_nch(bt->max_kv_len);
   char* w = (char*)ws;
-  a.hist = (uint32_t*)(w + L.hist);
-  a.bg = (uint32_t*)(w + L.bg);
-  a.cnt = (uint32_t*)(w + L.cnt);
-  a.bits = (uint32_t*)(w + L.bits);
-  a.slots = (uint64_t*)(w + L.slots);
+  char* o = w + ((ws_bytes - L.others) & ~(size_t)255);   // >= w + L.hist
+  a.hist = (uint32_t*)w;
+  a.bg = (uint32_t*)(o + L.bg);
+  a.cnt = (uint32_t*)(o + L.cnt);
+  a.bits = (uint32_t*)(o + L.bits);
+  a.slots = (uint64_t*)(o + L.slots);
   *out = a;
   return DSA_OK;
 }

@@ -205,3 +205,26 @@ def test_named_prefill_sampled_tokens():
     rng = np.random.default_rng(31)
     toks = np.unique(np.concatenate([[0, 1, 2047, 4095], rng.integers(0, 4096, 4)]))
     run_e2e(wl, token_subset=toks)
+
+
+def test_topk_workspace_reuse_across_calls():
+    """A workspace is zero-filled once: every call must leave its histograms cleared, so a call
+    on a second workload through the same workspace selects exactly what a fresh one does (fused
+    and standalone paths, rows of different lengths and batch sizes)."""
+    a = Gpu(make(Spec("reuse_a", 7401, [9000, 70000, 3000], [2, 1, 1], k=2048, Hq=16)))
+    b = Gpu(make(Spec("reuse_b", 7402, [66000, 5000], [1, 2], k=2048, Hq=16)))
+    # sized with the largest token count and the longest row of the two calls
+    need = dsa.dsa_topk_workspace_size(max(a.wl.T, b.wl.T),
+                                       max(a.batch.max_kv_len, b.batch.max_kv_len), 2048)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    log("case topk workspace reuse")
+    _, idx_a = a.indexer_topk(ws=ws)
+    _, idx_b = b.indexer_topk(ws=ws)
+    _, idx_b_fresh = b.indexer_topk()
+    assert torch.equal(idx_b, idx_b_fresh)
+    _, idx_a2 = a.indexer_topk(ws=ws)
+    assert torch.equal(idx_a2, idx_a)
+    sb = b.scores()
+    assert torch.equal(dsa.dsa_topk(b.batch, sb, 2048, ws=ws), idx_b_fresh)
+    assert torch.equal(dsa.dsa_topk(b.batch, sb, 2048, ws=ws), idx_b_fresh)
+    assert not ws[: 4 * 2048 * 4 * max(a.wl.T, b.wl.T)].any(), "histograms left non-zero"
