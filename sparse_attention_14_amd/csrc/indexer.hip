@@ -440,12 +440,24 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   }
   if constexpr (!DOTS) {
     __syncthreads();
+    // With the top-k's first radix pass fused (a.hist): a histogram of the top 11 key bits of
+    // this chunk's scores per token, in LDS (reusing the key buffer, free after the barrier
+    // above), taken from the values as they are stored; its non-zero bins are then added to
+    // one of the token's histogram shards.  Rows with at most hist_k valid keys get none.
+    uint32_t* hl = reinterpret_cast<uint32_t*>(kl);
+    static_assert(G * kHistBins * 4 <= KB, "histogram does not fit the key buffer");
+    if (a.hist) {
+      for (int i = threadIdx.x * 4; i < G * kHistBins; i += NT * 4)
+        *reinterpret_cast<uint4*>(hl + i) = uint4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
     // coalesced score stores, times the key scales: token j of the group, keys chunk0 ..
-    // min(chunk0 + kCK, p_j + 1); the stored value also feeds the histogram below
+    // min(chunk0 + kCK, p_j + 1)
     for (int j = 0; j < G; ++j) {
       const int tj = q_lo + j;
       if (tj >= q_hi) break;
       const int n = min(kCK, pg[j] + 1 - chunk0);
+      const bool hj = a.hist && pg[j] + 1 > a.hist_k;
       float* dst = a.scores + (long)tj * a.ld + chunk0;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
@@ -453,32 +465,25 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
         if (e < n) {
           const float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
           const float v = scl[j][e] * ks;
-          scl[j][e] = v;
           dst[e] = v;
+          if (hj) atomicAdd(&hl[j * kHistBins + (order_key(v) >> 21)], 1u);
         }
       }
     }
     if (a.hist) {
-      // The top-k's first radix pass, fused: histogram of the top 11 key bits of this chunk's
-      // scores per token (LDS, reusing the key buffer), non-zero bins added to one of the
-      // token's histogram shards.  Rows with at most hist_k valid keys get no histogram.
-      uint32_t* hl = reinterpret_cast<uint32_t*>(kl);
-      static_assert(G * kHistBins * 4 <= KB, "histogram does not fit the key buffer");
-      for (int i = threadIdx.x; i < G * kHistBins; i += NT) hl[i] = 0u;
       __syncthreads();
-      for (int j = 0; j < G; ++j) {
-        const int tj = q_lo + j;
-        if (tj >= q_hi) break;
-        if (pg[j] + 1 <= a.hist_k) continue;
-        const int n = min(kCK, pg[j] + 1 - chunk0);
-        for (int e = threadIdx.x; e < n; e += NT) atomicAdd(&hl[j * kHistBins + (order_key(scl[j][e]) >> 21)], 1u);
-      }
-      __syncthreads();
-      for (int i = threadIdx.x; i < G * kHistBins; i += NT) {
+      // eight consecutive bins per thread and step; only non-zero bins reach global memory
+      uint32_t* gh = a.hist + (long)blockIdx.x % kHistShards * kHistBins;
+      for (int i = threadIdx.x * 8; i < G * kHistBins; i += NT * 8) {
         const int j = i / kHistBins;
-        const uint32_t c = hl[i];
-        if (c && q_lo + j < q_hi)
-          atomicAdd(&a.hist[((long)(q_lo + j) * kHistShards + blockIdx.x % kHistShards) * kHistBins + (i % kHistBins)], c);
+        if (q_lo + j >= q_hi) continue;
+        const uint4 c0 = *reinterpret_cast<const uint4*>(hl + i);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(hl + i + 4);
+        const uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        uint32_t* dstb = gh + (long)(q_lo + j) * kHistShards * kHistBins + (i % kHistBins);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c[q]) atomicAdd(dstb + q, c[q]);
       }
     }
   }
