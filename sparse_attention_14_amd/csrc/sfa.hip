@@ -117,25 +117,34 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   int4 iv[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) iv[kb] = *reinterpret_cast<const int4*>(sidx + key0 + 16 * kb + 4 * g);
-  // all 36 K fragments are requested before the first MFMA (LDS latency is a few hundred
-  // cycles under load); the scheduling barrier keeps the compiler from interleaving them
-  v8bf k0[18], k1[18];
+  // K fragments in the order the MFMAs consume them (key block 0 and 1 of each 32-dim step).
+  // One wave keeps at most ~15 LDS reads in flight and reads 1 KiB per b128 instruction at
+  // ~46 B/clk, more than an MFMA's 16 cycles, so the schedule below keeps a window of reads
+  // ahead of the MFMAs (issue kPre reads, then alternate one MFMA and one read): the MFMAs
+  // run under the reads instead of after them.  Four independent accumulation chains (two per
+  // key block) keep the matrix core's issue rate, not its latency, the limit.
+  v8bf kf[36];
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
-    k0[ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(c16, 4 * ks + g));
-    k1[ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(16 + c16, 4 * ks + g));
+    kf[2 * ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(c16, 4 * ks + g));
+    kf[2 * ks + 1] = *reinterpret_cast<const v8bf*>(tile + tile_off(16 + c16, 4 * ks + g));
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // four independent accumulation chains (two per key block): a chain of dependent MFMAs is
-  // bound by their latency, four chains by the matrix core's issue rate
   v4f sa[2][2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) sa[0][c] = sa[1][c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
-    sa[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[ks], qf[ks], sa[0][ks & 1], 0, 0, 0);
-    sa[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[ks], qf[ks], sa[1][ks & 1], 0, 0, 0);
+    sa[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * ks], qf[ks], sa[0][ks & 1], 0, 0, 0);
+    sa[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * ks + 1], qf[ks], sa[1][ks & 1], 0, 0, 0);
   }
+  constexpr int kPre = 12;                 // reads ahead of the first MFMA (2 index + 10 K)
+  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+  for (int i = 0; i < 38 - kPre; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 36 - (38 - kPre), 0);
   const v4f s0 = sa[0][0] + sa[0][1], s1 = sa[1][0] + sa[1][1];
   // unused slots and keys past the split's end carry index -1 (the prologue pads the index
   // stage to whole tiles)
@@ -317,22 +326,25 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const int nt = (nkeys + kKT - 1) / kKT;
   const int role = __builtin_amdgcn_readfirstlane(wave < 2 ? 0 : (wave < 4 ? 1 : 2));  // score, loader, value
   // Loader wave lw gathers 1-KiB pieces J = lw + 2 it (it < 18) of tile i into ring slot i % 4.
-  // Rows past nkeys load clamped, valid rows whose keys are masked.  The per-lane offsets of the
-  // next tile are read ahead (offs), so a tile's loads issue right after the barrier.
-  uint32_t offs[18];
-  auto tile_offsets = [&](int i) {
-    // opaque lane id: keeps the per-load offsets from being hoisted out of the tile loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+  // A lane's piece it is always row prow[it] of the tile at (swizzled) byte pcol[it] of the
+  // row, so only the row's cache index changes from tile to tile; the index stage is padded
+  // with -1 to whole tiles (read as row 0: any valid row, masked).  The per-lane offsets of
+  // the next tile are read ahead (offs), so a tile's loads issue right after the barrier.
+  uint32_t offs[18], prow[18], pcol[18];
+  auto piece_rows = [&]() {
 #pragma unroll
     for (int it = 0; it < 18; ++it) {
-      const int J = (wave - 2) + 2 * it;
-      const int o = J * 1024 + ln * 16;
+      const int o = ((wave - 2) + 2 * it) * 1024 + lane * 16;
       const int r = o / kRowB;
-      const int c = ((o % kRowB) >> 4) ^ (r & 7);
-      const int key = min(i * kKT + r, nkeys - 1);
-      const int ix = max(sidx[key], 0);                // unused slot: any valid row (masked)
-      offs[it] = (uint32_t)ix * row_bytes + (uint32_t)c * 16u;
+      prow[it] = (uint32_t)r;
+      pcol[it] = (uint32_t)((((o % kRowB) >> 4) ^ (r & 7)) << 4);
+    }
+  };
+  auto tile_offsets = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < 18; ++it) {
+      const int ix = max(sidx[i * kKT + (int)prow[it]], 0);
+      offs[it] = (uint32_t)ix * row_bytes + pcol[it];
     }
   };
   auto issue_tile = [&](int i) {
@@ -369,6 +381,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
     return;
   }
   if (role == 1) {
+    piece_rows();
     tile_offsets(0);
     issue_tile(0);
     if (nt > 1) { tile_offsets(1); issue_tile(1); }
