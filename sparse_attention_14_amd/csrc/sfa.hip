@@ -410,45 +410,57 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   lds_barrier();                                       // running max and sum published
   const int ow = wave - 4;
 
-  // ---- epilogue: lane holds O^T[d = 128 ow + 16 mb + 4 g + e][head h0 + 16 nb + c16]
+  // ---- epilogue: lane holds O^T[d = 128 ow + 16 mb + 4 g + e][head h0 + 16 nb + c16].
+  // The scaled rows go through LDS (ring slot 0: every tile has been consumed and no gather is
+  // in flight) so that each head's 1 KiB row is stored by one wave instruction of 16 bytes per
+  // lane, instead of 16 strided 32-byte pieces per instruction.  Only the value waves are left
+  // in the workgroup (the others have ended), so the barrier below waits for them alone.
+  constexpr int kOP = kDv * 2 + 16;                    // LDS row pitch: rows in distinct banks
+  static_assert(32 * kOP <= kTileB, "the output rows do not fit a ring slot");
+  unsigned char* ot = ring;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int hl = 16 * nb + c16;
     const int h = h0 + hl;
     if (h >= a.Hq) continue;
     const float mh = fin[0][hl], lh = fin[1][hl];
+    float inv;
     if constexpr (FINAL) {
       const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
       const float M = fmaxf(mh, sk);
       const float f = mh == -INFINITY ? 0.f : exp2f(mh - M);
       const float den = lh * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
-      const float inv = den > 0.f ? f / den : 0.f;
-      u16* orow = a.out + ((long)t * a.Hq + h) * kDv + 128 * ow + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
-        pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
-        *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
-      }
+      inv = den > 0.f ? f / den : 0.f;
     } else {
       // the split's own softmax average O / l (a convex combination of value rows) in bf16;
       // the merge weighs it by 2^(m - M) l in fp32
-      const long base = ((long)t * a.n_split + split) * a.Hq + h;
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      u16* orow = a.ws_o + base * kDv + 128 * ow + 4 * g;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
-        pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
-        *reinterpret_cast<uint2*>(orow + 16 * mb) = pk;
-      }
+      inv = lh > 0.f ? 1.f / lh : 0.f;
       if (ow == 0 && g == 0) {
+        const long base = ((long)t * a.n_split + split) * a.Hq + h;
         a.ws_ml[base * 2 + 0] = mh;
         a.ws_ml[base * 2 + 1] = lh;
       }
     }
+    unsigned char* orow = ot + hl * kOP + (128 * ow + 4 * g) * 2;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
+      pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * mb) = pk;
+    }
+  }
+  lds_barrier();
+  // 32 rows x 64 pieces of 16 bytes over the 256 value-wave threads; row hl = piece / 64
+  u16* obase = FINAL ? a.out + ((long)t * a.Hq + h0) * kDv
+                     : a.ws_o + (((long)t * a.n_split + split) * a.Hq + h0) * kDv;
+  const int vt = tid - 256;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int piece = vt + 256 * i, hl = piece >> 6, c = piece & 63;
+    if (h0 + hl < a.Hq)
+      *reinterpret_cast<uint4*>(obase + (long)hl * kDv + c * 8) =
+          *reinterpret_cast<const uint4*>(ot + hl * kOP + c * 16);
   }
 }
 
