@@ -147,25 +147,34 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
   const int tid = threadIdx.x;
   const int p = a.q_pos[t];
   const float4 v = load4(a.scores + (long)t * a.ld, a.ld, ch);
+  // the upper half of every shard first (digits 1024..2047: keys of scores >= +0); the k-th
+  // largest score of a row is positive in practice, and the lower half is loaded only when
+  // the upper half holds fewer than k keys
+  static_assert(kBins == 2 * kNT, "one digit of each half per thread");
   const uint32_t* gh = a.hist + (long)t * kShards * kBins;
-  uint32_t hv[kShards][kBins / kNT];
+  uint32_t hv[kShards];
 #pragma unroll
-  for (int sd = 0; sd < kShards; ++sd)
-#pragma unroll
-    for (int j = 0; j < kBins / kNT; ++j) hv[sd][j] = gh[sd * kBins + tid + j * kNT];
+  for (int sd = 0; sd < kShards; ++sd) hv[sd] = gh[sd * kBins + kNT + tid];
   issue_fence();
   const int k = a.k;
   if (p + 1 <= k || ch * kChunk > p) return;             // short rows: finalize writes them
+  uint32_t x = 0;
 #pragma unroll
-  for (int j = 0; j < kBins / kNT; ++j) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int sd = 0; sd < kShards; ++sd) x += hv[sd][j];
-    h[tid + j * kNT] = x;
-  }
+  for (int sd = 0; sd < kShards; ++sd) x += hv[sd];
+  h[kNT + tid] = x;
+  h[tid] = 0u;
   if (tid < kCW) bw[tid] = 0u;
+  if (tid == 0) res[0] = 0xFFFFFFFFu;
   __syncthreads();
   find_digit_desc<kNT>(h, (uint32_t)k, sh, res);
+  if (res[0] == 0xFFFFFFFFu) {                            // block-uniform: the lower half too
+    uint32_t y = 0;
+#pragma unroll
+    for (int sd = 0; sd < kShards; ++sd) y += gh[sd * kBins + tid];
+    h[tid] = y;
+    __syncthreads();
+    find_digit_desc<kNT>(h, (uint32_t)k, sh, res);
+  }
   const uint32_t b1 = res[0];
   const int e0 = ch * kChunk + 4 * tid;
   const float f[4] = {v.x, v.y, v.z, v.w};

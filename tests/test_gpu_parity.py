@@ -93,6 +93,8 @@ def _topk_case(rng, T, L, k, kind):
         s = rng.standard_normal((T, L)).astype(np.float32)
     elif kind == "ties":          # few distinct values: many exact ties at the threshold
         s = rng.integers(-3, 4, (T, L)).astype(np.float32)
+    elif kind == "negative":      # every score below zero: the k-th key is in the lower digits
+        s = (-1.0 - np.abs(rng.standard_normal((T, L)))).astype(np.float32)
     elif kind == "zeros":         # +0 and -0 only
         s = np.where(rng.random((T, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
     else:                         # narrow band: candidates crowd the threshold digit
@@ -100,7 +102,7 @@ def _topk_case(rng, T, L, k, kind):
     return s
 
 
-@pytest.mark.parametrize("kind", ["random", "ties", "zeros", "narrow"])
+@pytest.mark.parametrize("kind", ["random", "ties", "negative", "zeros", "narrow"])
 def test_topk_exact_on_identical_scores(rng, kind):
     """Same fp32 scores on both sides: the selected sets must be identical (ties -> lower
     positions), for long rows, rows shorter than k and rows of exactly k."""
