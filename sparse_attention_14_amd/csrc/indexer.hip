@@ -472,18 +472,14 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
     }
     if (a.hist) {
       __syncthreads();
-      // eight consecutive bins per thread and step; only non-zero bins reach global memory
+      // consecutive bins in consecutive lanes, so that a wave's atomics fall in few lines; only
+      // non-zero bins reach global memory
       uint32_t* gh = a.hist + (long)blockIdx.x % kHistShards * kHistBins;
-      for (int i = threadIdx.x * 8; i < G * kHistBins; i += NT * 8) {
+      for (int i = threadIdx.x; i < G * kHistBins; i += NT) {
         const int j = i / kHistBins;
-        if (q_lo + j >= q_hi) continue;
-        const uint4 c0 = *reinterpret_cast<const uint4*>(hl + i);
-        const uint4 c1 = *reinterpret_cast<const uint4*>(hl + i + 4);
-        const uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        uint32_t* dstb = gh + (long)(q_lo + j) * kHistShards * kHistBins + (i % kHistBins);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (c[q]) atomicAdd(dstb + q, c[q]);
+        const uint32_t c = hl[i];
+        if (c && q_lo + j < q_hi)
+          atomicAdd(gh + (long)(q_lo + j) * kHistShards * kHistBins + (i % kHistBins), c);
       }
     }
   }
