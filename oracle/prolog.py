@@ -22,7 +22,9 @@ Readings (where the pages leave a step open):
   * round() is round-half-to-even; amax == 0 gives scale 0 and all-zero codes.
   * The fp32 scale is used for the codes; the stored scale is that value rounded to the
     scale dtype (fp16 by [PRO], or fp32).
-Pins: tests/test_oracle_prolog.py.
+Pins: tests/test_oracle_prolog.py (each step alone) and tests/test_oracle_compose.py (the
+chain's order through closed-form unit-vector cases; the per-token rotary broadcast over
+the query heads).
 """
 import numpy as np
 

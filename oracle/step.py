@@ -7,6 +7,9 @@ needs trained projection weights and is not part of this path; its outputs are i
 The cache state: every cache row's key has gone through the prolog (earlier steps wrote
 the old rows; this step writes the rows of its own query tokens), so each query token
 sees positions 0 .. p_t, itself included.
+Pins: tests/test_oracle_compose.py (the step against a brute-force walk through the
+definitions; every cache row and query token quantized with the rotary table of its own
+position).
 """
 import numpy as np
 

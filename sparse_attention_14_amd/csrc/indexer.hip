@@ -566,6 +566,9 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   if (ld < bt->max_kv_len) return fail(DSA_ERR_INVALID_ARG, "%s: ld (%ld) < max_kv_len (%d)", fn, ld, bt->max_kv_len);
   if (!want_dots && (ld % 4)) return fail(DSA_ERR_INVALID_ARG, "%s: ld must be a multiple of 4", fn);
   if (((uintptr_t)q | (uintptr_t)k) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q/k codes must be 16-byte aligned", fn);
+  // the token rows of w and q_scale are read as whole dwords
+  if (!want_dots && (((uintptr_t)qs | (uintptr_t)w) & 15))
+    return fail(DSA_ERR_INVALID_ARG, "%s: q_scale and w must be 16-byte aligned", fn);
 
   dsa::IdxArgs a{};
   a.q_start = bt->q_start; a.q_pos = bt->q_pos; a.kv_start = bt->kv_start;

@@ -194,11 +194,18 @@ def run_e2e(wl, token_subset=None, check_dots=False):
     check_scores(sc[torch.as_tensor(toks, device="cuda")], os_rows, wl.q_pos[toks])
     oi = oracle.topk_select(os_rows, sp.k)
     check_topk(idx[torch.as_tensor(toks, device="cuda")], oi, os_rows, wl.q_pos[toks], sp.k)
-    oo = oracle.sparse_attention(wl.q[toks], wl.kv, oi, wl.q_seq[toks], wl.kv_start, wl.sink, wl.scale)
+    gout = out[torch.as_tensor(toks, device="cuda")]
     gsel = idx.cpu().numpy()[toks]
+    # stage isolation: the oracle attention on the GPU's own selection, every compared token
+    og = oracle.sparse_attention(wl.q[toks], wl.kv, gsel, wl.q_seq[toks], wl.kv_start, wl.sink, wl.scale)
+    check_sfa(gout, og, what=f"attention on the GPU selection ({len(toks)} tokens)")
+    # end to end: the oracle's own selection, on the tokens whose selections are identical
     same = [i for i in range(len(toks)) if np.array_equal(gsel[i], oi[i])]
     log(f"  {len(same)}/{len(toks)} tokens with identical selections")
-    check_sfa(out[torch.as_tensor(toks, device="cuda")], oo, tokens=same, what="end-to-end attention")
+    assert same, "no token with an identical selection: the end-to-end comparison is empty"
+    oo = oracle.sparse_attention(wl.q[toks][same], wl.kv, oi[same], wl.q_seq[toks][same], wl.kv_start,
+                                 wl.sink, wl.scale)
+    check_sfa(gout[torch.as_tensor(same, device="cuda")], oo, what="end-to-end attention")
     if check_dots and sp.code == "i8":
         dots = dsa.dsa_indexer_dots_i32(g.batch, sp.H, sp.D, g.q_codes, g.k_cache).cpu().numpy()
         od = oracle.indexer_dots(oq["q_codes"][toks], oq["k_codes"], "i8", wl.q_seq[toks],

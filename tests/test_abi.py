@@ -67,6 +67,12 @@ def test_validation_errors_before_any_device_call():
     assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, P, P, P, P, P, 100, None) == L.DSA_ERR_INVALID_ARG
     # null data pointer
     assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, P, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    # misaligned q_scale / w rows (an odd storage offset of a torch view)
+    Q2 = ctypes.c_void_p(0x1002)
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, Q2, P, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    assert b"aligned" in lib.dsa_last_error()
+    assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, P, Q2, P, P, P, 65536, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_topk(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, P, P, Q2, P, P, P, 65536, 2048, P, P, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
     # top-k: k out of range, workspace too small
     assert lib.dsa_topk(ctypes.byref(b), P, 65536, 4096, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
     assert lib.dsa_topk(ctypes.byref(b), P, 65536, 2048, P, P, 16, None) == L.DSA_ERR_WORKSPACE

@@ -200,12 +200,30 @@ def test_named_workload_end_to_end(cfg_id):
     run_e2e(workloads.named(cfg_id), check_dots=(cfg_id == 1))
 
 
+def prefill_sample(wl, n_random=40, seed=31):
+    """Tokens of the prefill chunk compared with the oracle: the first and last, the two tokens
+    on each side of every 512-key boundary (the indexer's key chunks), those on each side of
+    every 4096-position boundary (the top-k's score chunks), and seeded random ones."""
+    T = wl.T
+    p0 = int(wl.q_pos[0])
+    picks = {0, 1, T - 2, T - 1}
+    for period in (512, 4096):
+        for p in range(p0 - p0 % period, p0 + T + 1, period):
+            for q in (p - 2, p - 1, p, p + 1):
+                if p0 <= q < p0 + T:
+                    picks.add(q - p0)
+    rng = np.random.default_rng(seed)
+    picks.update(int(x) for x in rng.integers(0, T, n_random))
+    return np.array(sorted(picks))
+
+
 def test_named_prefill_sampled_tokens():
     """Prefill chunk (4096 new tokens on a 61440-token cache): the full GPU step, compared with
-    the oracle on sampled tokens (first, last, and seeded random ones)."""
+    the oracle on >= 64 sampled tokens (chunk boundaries of the indexer and the top-k, first,
+    last and seeded random ones)."""
     wl = workloads.named(3)
-    rng = np.random.default_rng(31)
-    toks = np.unique(np.concatenate([[0, 1, 2047, 4095], rng.integers(0, 4096, 4)]))
+    toks = prefill_sample(wl)
+    assert len(toks) >= 64
     run_e2e(wl, token_subset=toks)
 
 
