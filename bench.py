@@ -56,25 +56,27 @@ def parse():
     return ap.parse_args()
 
 
-COUNTER_FILE = os.path.join(ROOT, "profiles", "sfa_kernel_decode_b4_mtp1_L65536_counters.md")
+def counter_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"step_kernels_{workload}_counters.md")
 
 
 def kernel_source_hash() -> str:
-    """sha256 of the attention kernel's sources: counter-derived traffic is reported only
-    while it still describes the kernel being timed."""
+    """sha256 of the kernel sources: counter-derived traffic is reported only while it still
+    describes the kernels being timed."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("sfa.hip", "common.h"):
+    for f in sorted(f for f in os.listdir(os.path.join(ROOT, "sparse_attention_14_amd", "csrc"))
+                    if f.endswith((".hip", ".h"))):
         with open(os.path.join(ROOT, "sparse_attention_14_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str):
+def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on
     the current sources (line: `traffic_bytes_per_launch <kernel> <bytes> <source sha256>`)."""
     try:
-        with open(COUNTER_FILE) as fh:
+        with open(counter_file(workload)) as fh:
             for line in fh:
                 f = line.strip().strip("`").split()
                 if len(f) == 4 and f[0] == "traffic_bytes_per_launch" and f[1] == kernel:
@@ -235,20 +237,35 @@ def main():
         for s in sets:
             assert torch.equal(s.buf.out, ref), f"graph replay {rep} differs from eager"
 
-    # warm-up and timed region: K steps = K / R replays of the R-step graph
-    reps_w = max(1, args.warmup // R)
-    reps = max(1, int(round(args.steps / R)))
+    # warm-up and timed region: whole replays of the R-step graph, at least 8 of them, each
+    # bracketed by its own pair of events (per-replay samples for the median and spread); the
+    # value is the mean over every timed step
+    reps_w = max(1, int(np.ceil(args.warmup / R)))
+    reps = max(8, int(np.ceil(args.steps / R)))
     K = reps * R
     replay(g_step, reps_w)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    replay(g_step, reps)
-    e1.record(stream)
+    evs[0].record(stream)
+    for i in range(reps):
+        replay(g_step, 1)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    us_step = e0.elapsed_time(e1) * 1000.0 / K
+    us_step = evs[0].elapsed_time(evs[-1]) * 1000.0 / K
+    per_rep = np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 / R for i in range(reps)])
+
+    # warm: the same step R times on one input set (everything it touches may sit in the MALL)
+    g_warm = capture(lambda s: step(sets[0]))
+    replay(g_warm, 2)
+    torch.cuda.synchronize()
+    a_w, b_w = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_w.record(stream)
+    replay(g_warm, 4)
+    b_w.record(stream)
+    torch.cuda.synchronize()
+    warm_us = a_w.elapsed_time(b_w) * 1000.0 / (4 * R)
 
     # paged caches (Page Attention blocks of 128 rows, shuffled): copies of every set's K and
     # KV caches, for the paged calls' stage timing; they must select and attend exactly as the
@@ -311,13 +328,31 @@ def main():
 
     idx_tops = idx_ops / (stage_us["indexer"] * 1e-6) / 1e12
     sfa_gbps = n_sel * 1152 / (stage_us["sfa"] * 1e-6) / 1e9
-    # roofline of the dominant kernel: among the single-kernel calls, the longest per launch;
-    # algorithmic bytes per launch (the split stage: gathered rows, q, indices)
-    single = {"indexer": ("dsa::indexer_kernel", b_indexer),
-              "sfa_split": ("dsa::sfa_kernel", n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4)}
+    # roofline of the dominant kernel: among the single-kernel calls, the longest per launch.
+    # Decode shapes are bound by HBM (algorithmic bytes per launch: the indexer's keys, scales,
+    # q/w and scores; the attention split's gathered rows, q and indices); the prefill chunk
+    # (many query tokens per sequence) by the matrix cores (int8 indexer ops, bf16 attention
+    # flops), where the keys and gathered rows come from the caches
+    prefill = wl.max_q_per_seq > 4
+    idx_peak = INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS
+    single = {"indexer": ("dsa::indexer_kernel", b_indexer, idx_ops, idx_peak),
+              "sfa_split": ("dsa::sfa_kernel", n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4,
+                            sfa_flops, BF16_PEAK_TFLOPS)}
     dominant = max(single, key=lambda n: stage_us[n])
-    kernel_name, dom_bytes = single[dominant]
-    dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
+    kernel_name, dom_bytes, dom_ops, dom_peak = single[dominant]
+    dom_sec = stage_us[dominant] * 1e-6
+    if prefill:
+        roof = {"kernel": kernel_name, "call": dominant, "bound": "mfma",
+                "achieved": round(dom_ops / dom_sec / 1e12, 1), "peak": dom_peak,
+                "unit": "TOP/s" if dominant == "indexer" and cfg.code == "i8" else "TFLOP/s",
+                "frac": round(dom_ops / dom_sec / 1e12 / dom_peak, 4), "traffic": None,
+                "ops_per_launch": dom_ops, "avg_launch_us": round(stage_us[dominant], 3)}
+    else:
+        dom_gbps = dom_bytes / dom_sec / 1e9
+        roof = {"kernel": kernel_name, "call": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": recorded_traffic(kernel_name, sp.name), "bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(stage_us[dominant], 3)}
 
     result = {
         "metric": "DSA decode us/step at B=4,64K ctx; indexer int8 TOPS; SFA gathered-KV GB/s",
@@ -337,16 +372,23 @@ def main():
                    "topk": k, "attn_heads": Hq, "d_qk": 576, "d_v": 512,
                    "prolog": "rope+hadamard+quant" if sp.full_prolog else "quant",
                    "rotating_input_sets": R, "per_step_hbm_bytes": step_bytes},
+        "timing": {"replays": reps, "steps_per_replay": R,
+                   "median_us": round(float(np.median(per_rep)), 3),
+                   "p10_us": round(float(np.percentile(per_rep, 10)), 3),
+                   "p90_us": round(float(np.percentile(per_rep, 90)), 3),
+                   "warm_us": round(warm_us, 3),
+                   "note": "value = mean over every timed step; median/p10/p90 over the per-replay "
+                           "means of R rotating-input steps; warm = R steps on one input set"},
         "step_roofline_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "stage_us": {n: round(v, 3) for n, v in stage_us.items()},
-        "indexer_tops": round(idx_tops, 2),
-        "indexer_tops_frac": round(idx_tops / (INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS), 4),
+        # indexer ops (2 H D per visible (token, key)) per second of the indexer call, against the
+        # dense int8 (or, for e4m3 codes contracted on bf16, the bf16) MFMA peak
+        ("indexer_tops_prefill_shape" if prefill else "indexer_tops_decode_shape"): round(idx_tops, 2),
+        "indexer_tops_frac": round(idx_tops / idx_peak, 4),
         "sfa_gathered_GBps": round(sfa_gbps, 1),
         "sfa_gathered_frac": round(sfa_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": kernel_name, "call": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic(kernel_name), "bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(stage_us[dominant], 3)},
+        "sfa_tflops": round(sfa_flops / (stage_us["sfa"] * 1e-6) / 1e12, 1),
+        "roofline": roof,
         "wall_s_timed": round(wall, 4),
         "projections": proj,
     }
@@ -412,38 +454,61 @@ def projections_stage(stream, dev) -> dict:
             "rotating_weight_sets": n_sets}
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, budget_s: float, max_tokens: int = 32) -> dict:
     """The oracle's decode step on the host cores (prolog of the new tokens and rows, indexer
-    over every visible key, top-k, attention), repeated while within the time budget."""
+    over every visible key, top-k, attention), repeated while within the time budget.  A batch
+    of more than `max_tokens` query tokens is sampled: the oracle runs on a seeded subset of its
+    tokens and the time is scaled by T / subset (every token's work is independent)."""
     import oracle
     from oracle.step import prolog_inputs_f64
     from threadpoolctl import threadpool_info
     sp = wl.spec
     oq = oracle.step.quantize_workload(wl)          # cache state from earlier steps (untimed)
     q_in, k_in = prolog_inputs_f64(wl)
-    rows = wl.new_rows()
+    toks = np.arange(wl.T)
+    if wl.T > max_tokens:
+        toks = np.sort(np.random.default_rng(5).choice(wl.T, max_tokens, replace=False))
+    rows = wl.new_rows()[toks]
     rope = sp.rope_dim if sp.full_prolog else 0
+    sub = lambda a: None if a is None else a[toks]
     n, t_tot = 0, 0.0
-    while t_tot < budget_s and n < 50:
+    while (t_tot < budget_s and n < 50) or n == 0:
         t0 = time.perf_counter()
-        nq = oracle.indexer_prolog(q_in, k_in[rows], wl.q_cos, wl.q_sin,
+        nq = oracle.indexer_prolog(q_in[toks], k_in[rows], sub(wl.q_cos), sub(wl.q_sin),
                                    None if wl.k_cos is None else wl.k_cos[rows],
                                    None if wl.k_sin is None else wl.k_sin[rows], rope,
                                    sp.rope_offset, sp.rope_interleaved, sp.full_prolog, sp.code,
                                    sp.scale_dt)
         oq["k_codes"][rows] = nq["k_codes"]
         oq["k_scale"][rows] = nq["k_scale"]
-        sc = oracle.indexer_scores(nq["q_codes"], nq["q_scale"], wl.w, oq["k_codes"], oq["k_scale"],
-                                   sp.code, wl.q_seq, wl.q_pos, wl.kv_start)
+        sc = oracle.indexer_scores(nq["q_codes"], nq["q_scale"], wl.w[toks], oq["k_codes"],
+                                   oq["k_scale"], sp.code, wl.q_seq[toks], wl.q_pos[toks], wl.kv_start)
         idx = oracle.topk_select(sc, sp.k)
-        oracle.sparse_attention(wl.q, wl.kv, idx, wl.q_seq, wl.kv_start, wl.sink, wl.scale)
+        oracle.sparse_attention(wl.q[toks], wl.kv, idx, wl.q_seq[toks], wl.kv_start, wl.sink, wl.scale)
         t_tot += time.perf_counter() - t0
         n += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(t_tot / n * 1e6, 1), "unit": "us/step", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n} full decode steps of the same workload ({wl.T} query tokens), "
-                      f"float64 numpy oracle, cache quantization excluded"}
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] + [1])
+    blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')})"
+                     for p in info if p.get("user_api") == "blas") or "unknown"
+    scale = wl.T / len(toks)
+    what = (f"{n} full decode steps of the same workload ({wl.T} query tokens)" if scale == 1 else
+            f"{n} steps over a seeded sample of {len(toks)} of the {wl.T} query tokens, time x {scale:g}")
+    return {"value": round(t_tot / n * scale * 1e6, 1), "unit": "us/step", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(), "blas": blas,
+            "sample": f"{what}, float64 numpy oracle, cache quantization excluded"}
 
 
 if __name__ == "__main__":
