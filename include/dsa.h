@@ -213,7 +213,8 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int
  * written as documented there) and then dsa_topk on those scores, with the same arguments,
  * results, workspace contract and errors.  The top-k's first radix pass (a histogram of the
  * top 11 key bits per row) is accumulated by the indexer workgroups, which saves one pass
- * over the scores and one launch.
+ * over the scores and one launch.  Batches of 256 or more query tokens (a prefill chunk) finish
+ * each row's selection in one workgroup of their own (one launch after the indexer).
  */
 dsa_status dsa_indexer_topk(const dsa_batch* batch, int32_t H, int32_t D,
                             dsa_dtype code_dtype, dsa_dtype scale_dtype,

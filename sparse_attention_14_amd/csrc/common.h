@@ -70,6 +70,57 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 constexpr int kHistBins = 2048;          // top-k radix histogram: the top 11 bits of the key
 constexpr int kHistShards = 4;           // copies of each row histogram (spread atomic traffic)
 
+// Inclusive prefix sum over the 64 lanes of a wave: four row shifts within each 16-lane row,
+// then the row broadcasts of lanes 15 and 31 (DPP, no LDS round trip).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sum over the NT threads of the block (one barrier); `total` gets the sum.
+// sh holds NT/64 words; consecutive uses of one sh must be separated by a barrier.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t x = sh[i];
+    before += i < w ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return before + inc - v;
+}
+
+// The digit holding the need-th largest element of an LDS histogram over kBins digits:
+// res[0] = digit, res[1] = elements in larger digits.  Ends with a barrier.
+template <int NT>
+__device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* res) {
+  constexpr int PER = kHistBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t loc[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { loc[j] = hist[kHistBins - 1 - (tid * PER + j)]; tot += loc[j]; }
+  uint32_t all;
+  uint32_t before = block_excl_scan<NT>(tot, sh, all);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (before < need && need <= before + loc[j]) { res[0] = kHistBins - 1 - (tid * PER + j); res[1] = before; }
+    before += loc[j];
+  }
+  __syncthreads();
+}
+
 // Flat workgroup id remapped so that consecutive logical ids land on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); logical id
 // w = xcd * per_xcd + slot keeps neighbours (which share data) in one L2.

@@ -499,6 +499,376 @@ static void launch_g(int G, const IdxArgs& a, dim3 grid, hipStream_t st) {
   else launch<4, NMB, D, FP8, DOTS>(a, grid, st);
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Streaming decode kernel (at most four query tokens per sequence).
+//
+// A workgroup of eight waves owns one sequence and a long span of its keys (SPAN keys, chosen on
+// the host so that about one workgroup per CU covers the batch).  Every wave is its own pipeline:
+// it takes every 8th (G <= 2) or 4th (G = 4, two token pairs) 32-key block of the span, streams
+// those blocks HBM -> LDS by direct loads through a private ring of NB slots (NB - 1 blocks in
+// flight), waits for them with its own vmcnt and never for another wave, and contracts each
+// block against the query codes of its tokens (the block is read once per CU whatever G is).
+// No barrier stands in the block loop, so the waves sharing a SIMD drift apart and one's
+// ReLU-weighted head sum (VALU) runs under the other's MFMAs.  The query codes, the head weights
+// and the query scales are staged once per workgroup (w * q_scale as a small LDS table).
+// Scores stay in LDS until the span is done; a final coalesced pass multiplies them by the key
+// scales (loaded before the stream, waited for only there), stores them and feeds the top-k
+// histogram.
+constexpr int kSNW = 8;                        // waves per workgroup
+// G x SPAN scores held in LDS (with the ring and the query codes: at most 160 KiB)
+__host__ __device__ constexpr int stream_scl(int G) { return G == 1 ? 8192 : 4096; }
+
+template <int G, int D>
+struct SShape {
+  static constexpr int HT = D == 128 ? 64 : 8;              // heads of the compiled shape
+  static constexpr int NMB = (HT + 31) / 32;                // 32-head M-blocks
+  static constexpr int CPR = D / 16;                        // 16-byte chunks per key row
+  static constexpr int NTW = G < 2 ? G : 2;                 // tokens per wave
+  static constexpr int BSTR = kSNW / (G / NTW);             // block stride of a wave
+  static constexpr int BB = 32 * D;                         // block bytes
+  static constexpr int NPB = BB / 1024;                     // 1-KiB DMA pieces per block
+  static constexpr int NB = D == 128 ? 3 : 6;               // ring slots per wave
+  static constexpr int SCL = stream_scl(G);
+  static constexpr int QB = G * HT * D;                     // query codes of the group
+  static constexpr int QR = (QB + 1023) / 1024 * 1024;      // their LDS region
+  static constexpr int KPT = SCL / G / (kSNW * 64);         // key scales per thread (max)
+  static_assert(NB >= 3 && NB - 2 <= 6, "ring depth");
+  static_assert(G * kHistBins * 4 <= kSNW * NB * BB, "histogram does not fit the ring");
+};
+
+// s_waitcnt vmcnt(P * n) for a runtime n in [0, 6]
+template <int P>
+__device__ __forceinline__ void wait_blocks_after(int n) {
+  switch (n) {
+    case 0: idx_wait_vm<0>(); break;
+    case 1: idx_wait_vm<P * 1>(); break;
+    case 2: idx_wait_vm<P * 2>(); break;
+    case 3: idx_wait_vm<P * 3>(); break;
+    case 4: idx_wait_vm<P * 4>(); break;
+    case 5: idx_wait_vm<P * 5>(); break;
+    default: idx_wait_vm<P * 6>(); break;
+  }
+}
+// 4 bytes at base + off (base wave-uniform in SGPRs) into LDS at lds_addr + 4 * lane
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, unsigned lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" :: "v"(off), "s"(base), "{m0}"(lds_addr));
+}
+// Sum of lane l and lane l ^ 32 (the two 16-head halves of an MFMA column), in every lane.
+__device__ __forceinline__ float add_half_swap(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+}
+
+struct StreamArgs {
+  IdxArgs a;
+  int span;              // keys per workgroup (a multiple of 32 * kSNW)
+};
+
+template <int G, int D, bool FP8, bool DOTS, bool SF16>
+__global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa) {
+  typedef SShape<G, D> S;
+  constexpr int NT = kSNW * 64;
+  constexpr int NTW = S::NTW;
+  const IdxArgs& a = sa.a;
+  const int SPAN = sa.span;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSNW * S::NB * S::BB];
+  __shared__ __attribute__((aligned(1024))) unsigned char qsm[S::QR];
+  __shared__ __attribute__((aligned(16))) float scl[DOTS ? 1 : S::SCL];
+  __shared__ __attribute__((aligned(16))) uint32_t wraw[G * S::HT / 2 > 64 ? G * S::HT / 2 : 64];
+  __shared__ __attribute__((aligned(16))) uint32_t sraw[G * S::HT * (SF16 ? 1 : 2) / 2 > 64 ? G * S::HT * (SF16 ? 1 : 2) / 2 : 64];
+  __shared__ __attribute__((aligned(16))) float wqt[G][S::HT];
+  __shared__ int sbt[S::SCL / G / 16 + 1];                    // paged: the span's block entries
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hv = lane >> 5, col = lane & 31;
+  const int b = blockIdx.y;
+  const int span0 = blockIdx.x * SPAN;
+  const int tw0 = (wave / S::BSTR) * NTW;                     // this wave's first token
+  const int blk0 = wave % S::BSTR;                             // ... and first block
+
+  // ---- batch metadata in one round trip (lane vectors, picked by lane) for small batches
+  int t0, nq, pg[G], maxp = -1;
+  long kv0;
+  if (a.B < 64 && a.T <= 64) {
+    const int qs_l = a.q_start[min(lane, a.B)];
+    const int qp_l = a.q_pos[min(lane, a.T - 1)];
+    const long kv_l = a.bt ? 0 : a.kv_start[min(lane, a.B - 1)];
+    t0 = __builtin_amdgcn_readlane(qs_l, b);
+    nq = min(__builtin_amdgcn_readlane(qs_l, b + 1) - t0, G);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      pg[j] = j < nq ? __builtin_amdgcn_readlane(qp_l, min(t0 + j, a.T - 1)) : -1;
+      maxp = max(maxp, pg[j]);
+    }
+    kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_l >> 32), b) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)kv_l, b));
+  } else {
+    t0 = a.q_start[b];
+    nq = min(a.q_start[b + 1] - t0, G);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      pg[j] = j < nq ? a.q_pos[t0 + j] : -1;
+      maxp = max(maxp, pg[j]);
+    }
+    kv0 = a.bt ? 0 : a.kv_start[b];
+  }
+  if (nq <= 0 || span0 > maxp) return;
+  const int nkeys = min(SPAN, maxp + 1 - span0);               // keys of the span in use
+  const int last_row = nkeys - 1;                              // span-relative clamp for loads
+  const int nblk = (nkeys + 31) / 32;                          // 32-key blocks of the span
+  const int nbw = blk0 < nblk ? (nblk - 1 - blk0) / S::BSTR + 1 : 0;   // this wave's blocks
+  const int H = a.H;
+
+  // paged: the span's block-table entries into LDS (blocks of >= 16 keys)
+  if (a.bt) {
+    const int nbe = (nkeys - 1 + (span0 & ((1 << a.bs_log2) - 1))) / (1 << a.bs_log2) + 1;
+    for (int i = tid; i < nbe; i += NT) sbt[i] = a.bt[(long)b * a.bps + (span0 >> a.bs_log2) + i];
+    __syncthreads();
+  }
+  auto cache_row = [&](int r) -> long {                        // r: span-relative key
+    if (!a.bt) return kv0 + span0 + r;
+    const int pos = span0 + r;
+    return ((long)sbt[(pos >> a.bs_log2) - (span0 >> a.bs_log2)] << a.bs_log2) + (pos & ((1 << a.bs_log2) - 1));
+  };
+
+  // ---- key scales of the span (waited for in the final pass only)
+  uint32_t ksraw[DOTS ? 1 : S::KPT];
+  if constexpr (!DOTS) {
+#pragma unroll
+    for (int i = 0; i < S::KPT; ++i) {
+      const long row = cache_row(min(tid + i * NT, last_row));
+      ksraw[i] = SF16 ? (uint32_t)((const u16*)a.k_scale)[row] : ((const uint32_t*)a.k_scale)[row];
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- DMA: query codes, head weights and query scales, then this wave's first NB - 1 blocks
+  const unsigned q_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)qsm;
+  {
+    const uint8_t* qsrc = uniform_ptr(a.q_codes + (long)t0 * H * D);
+    const int qbytes = nq * H * D;                             // tokens past nq: clamped copies
+    if constexpr (S::QB >= 1024) {
+      for (int j = wave; j < S::QB / 1024; j += kSNW)
+        dma16(qsrc, (uint32_t)min(j * 1024 + lane * 16, qbytes - 16), q_base + j * 1024);
+    } else {
+      for (int j = wave; j < (S::QB + 255) / 256; j += kSNW)
+        dma4(qsrc, (uint32_t)min(j * 256 + lane * 4, qbytes - 4), q_base + j * 256);
+    }
+    if constexpr (!DOTS) {
+      if (wave == kSNW - 1) {
+        const int wbytes = nq * H * 2;
+        const unsigned char* wsrc = uniform_ptr((const unsigned char*)a.w + (long)t0 * H * 2);
+        for (int j = 0; j < (G * S::HT * 2 + 255) / 256; ++j)
+          dma4(wsrc, (uint32_t)min(j * 256 + lane * 4, wbytes - 4),
+               (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)wraw + j * 256);
+        const int sb = SF16 ? 2 : 4;
+        const int sbytes = nq * H * sb;
+        const unsigned char* ssrc = uniform_ptr((const unsigned char*)a.q_scale + (long)t0 * H * sb);
+        for (int j = 0; j < (G * S::HT * sb + 255) / 256; ++j)
+          dma4(ssrc, (uint32_t)min(j * 256 + lane * 4, sbytes - 4),
+               (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)sraw + j * 256);
+      }
+    }
+  }
+  // Block i of this wave is span block blk0 + BSTR * i in ring slot i % NB.  Piece j of a block
+  // holds rows j * (1024 / D) + lrow; the lane's 16 bytes are chunk c of that row, stored at
+  // chunk c ^ (row % CPR) (the swizzle period divides 1024 / D, so the lane offset is the same in
+  // every piece and every block).
+  const int lrow = lane * 16 / D;
+  const int lchunk = (((lane * 16) % D) >> 4) ^ (lrow & (S::CPR - 1));
+  const uint32_t lane_off = (uint32_t)(lrow * D + lchunk * 16);
+  const unsigned wring = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring +
+                         (unsigned)(wave * S::NB * S::BB);
+  const uint8_t* kbase = uniform_ptr(a.bt ? a.k_cache : a.k_cache + (kv0 + span0) * D);
+  auto issue_block = [&](int i) {
+    const unsigned slot = wring + (unsigned)((i % S::NB) * S::BB);
+    const int r0 = (blk0 + S::BSTR * i) * 32;
+    if (!a.bt && r0 + 31 <= last_row) {
+#pragma unroll
+      for (int j = 0; j < S::NPB; ++j) dma16(kbase, (uint32_t)(r0 * D + j * 1024) + lane_off, slot + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::NPB; ++j) {
+        const int rr = min(r0 + j * (1024 / D) + lrow, last_row);
+        dma16(kbase, (uint32_t)((a.bt ? cache_row(rr) : (long)rr) * D + lchunk * 16), slot + j * 1024);
+      }
+    }
+  };
+  for (int i = 0; i < S::NB - 1 && i < nbw; ++i) issue_block(i);
+
+  // ---- staging: wait for the query, weights and scales (issued before the blocks), build
+  // w * q_scale, then move this wave's operands into registers
+  wait_blocks_after<S::NPB>(min(S::NB - 1, nbw));
+  idx_lds_barrier();
+  if constexpr (!DOTS) {
+    if (tid < G * S::HT) {
+      const int j = tid / S::HT, h = tid % S::HT;
+      const int jj = min(j, nq - 1);
+      const u16 wv = ((const u16*)wraw)[jj * H + h];
+      const float qsv = SF16 ? f16_bits_to_f32(((const u16*)sraw)[jj * H + h])
+                             : __uint_as_float(sraw[jj * H + h]);
+      wqt[j][h] = f16_bits_to_f32(wv) * qsv;
+    }
+    idx_lds_barrier();
+  }
+  KFrag<FP8, D> qf[NTW][S::NMB];
+  float wq[DOTS ? 1 : NTW][S::NMB][16];
+  int pt[NTW];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int ti = tw0 + u;
+    pt[u] = ti < nq ? pg[ti] : -1;
+#pragma unroll
+    for (int mb = 0; mb < S::NMB; ++mb) {
+      const int hr = min(32 * mb + col, S::HT - 1);
+      const unsigned char* qrow = qsm + (ti * S::HT + hr) * D;
+#pragma unroll
+      for (int q = 0; q < S::CPR / 2; ++q) {
+        const v4i w = *reinterpret_cast<const v4i*>(qrow + (hv * (S::CPR / 2) + q) * 16);
+        if constexpr (!FP8) {
+          qf[u][mb].v[q] = w;
+        } else {
+          qf[u][mb].v[2 * q] = fp8x8_to_bf16<D>(w[0], w[1]);
+          qf[u][mb].v[2 * q + 1] = fp8x8_to_bf16<D>(w[2], w[3]);
+        }
+      }
+      if (32 * mb + col >= S::HT) {
+#pragma unroll
+        for (int j = 0; j < (FP8 ? D / 16 : D / 32); ++j) qf[u][mb].v[j] = {};
+      }
+      if constexpr (!DOTS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (32 * mb + 8 * j >= S::HT) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wq[u][mb][4 * j + e] = 0.f;
+          } else {
+            const float4 v = *reinterpret_cast<const float4*>(&wqt[ti][32 * mb + 8 * j + 4 * hv]);
+            wq[u][mb][4 * j + 0] = v.x; wq[u][mb][4 * j + 1] = v.y;
+            wq[u][mb][4 * j + 2] = v.z; wq[u][mb][4 * j + 3] = v.w;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- the block loop: no barrier, each wave waits for its own loads only
+  for (int i = 0; i < nbw; ++i) {
+    wait_blocks_after<S::NPB>(min(S::NB - 2, nbw - 1 - i));   // block i landed
+    if (i + S::NB - 1 < nbw) issue_block(i + S::NB - 1);       // into the slot of block i - 1
+    const int key0 = (blk0 + S::BSTR * i) * 32;                // span-relative first key
+    if (span0 + key0 > maxp) break;                            // wave-uniform (never, by nbw)
+    const unsigned char* tile = ring + wave * S::NB * S::BB + (i % S::NB) * S::BB;
+    KFrag<FP8, D> kf;
+    {
+      v4i raw[S::CPR / 2];
+#pragma unroll
+      for (int q = 0; q < S::CPR / 2; ++q) {
+        const int cc = hv * (S::CPR / 2) + q;
+        raw[q] = *reinterpret_cast<const v4i*>(tile + col * D + ((cc ^ (col & (S::CPR - 1))) << 4));
+      }
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int q = 0; q < S::CPR / 2; ++q) kf.v[q] = raw[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < S::CPR / 2; ++q) {
+          kf.v[2 * q] = fp8x8_to_bf16<D>(raw[q][0], raw[q][1]);
+          kf.v[2 * q + 1] = fp8x8_to_bf16<D>(raw[q][2], raw[q][3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int ti = tw0 + u;
+      if (span0 + key0 > pt[u]) continue;                      // wave-uniform (pt = -1: no token)
+      if constexpr (DOTS) {
+        const int s = span0 + key0 + col;
+#pragma unroll
+        for (int mb = 0; mb < S::NMB; ++mb) {
+          const auto acc = mma_block<FP8, D>(qf[u][mb], kf);
+          if (s <= pt[u]) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int h = 32 * mb + 8 * (e >> 2) + 4 * hv + (e & 3);
+              if (8 * (e >> 2) + 32 * mb < S::HT && h < H)
+                a.dots[((long)(t0 + ti) * H + h) * a.ld + s] = (int32_t)acc[e];
+            }
+          }
+        }
+      } else {
+        float sum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < S::NMB; ++mb) {
+          const auto acc = mma_block<FP8, D>(qf[u][mb], kf);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (32 * mb + 8 * (e >> 2) >= S::HT) continue;      // compile-time: rows past H
+            float d;
+            if constexpr (FP8) d = fmaxf(acc[e], 0.f);
+            else d = (float)max(acc[e], 0);
+            sum = fmaf(wq[u][mb][e], d, sum);
+          }
+        }
+        sum = add_half_swap(sum);
+        if (hv == 0) scl[ti * SPAN + key0 + col] = sum;         // times the key scale when stored
+      }
+    }
+  }
+  if constexpr (!DOTS) {
+    __syncthreads();                                             // every stream has landed
+    // With the top-k's first radix pass fused (a.hist): a histogram of the top 11 key bits of
+    // the span's scores per token in LDS (the ring is free), its non-zero bins then added to
+    // one of the token's histogram shards.  Rows with at most hist_k valid keys get none.
+    uint32_t* hl = reinterpret_cast<uint32_t*>(ring);
+    if (a.hist) {
+      for (int i = tid * 4; i < G * kHistBins; i += NT * 4)
+        *reinterpret_cast<uint4*>(hl + i) = uint4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+    for (int j = 0; j < G; ++j) {
+      if (j >= nq) break;
+      const int n = min(nkeys, pg[j] + 1 - span0);
+      const bool hj = a.hist && pg[j] + 1 > a.hist_k;
+      float* dst = a.scores + (long)(t0 + j) * a.ld + span0;
+#pragma unroll
+      for (int i = 0; i < S::KPT; ++i) {
+        const int e = tid + i * NT;
+        if (e < n) {
+          const float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
+          const float v = scl[j * SPAN + e] * ks;
+          dst[e] = v;
+          if (hj) atomicAdd(&hl[j * kHistBins + (order_key(v) >> 21)], 1u);
+        }
+      }
+    }
+    if (a.hist) {
+      __syncthreads();
+      uint32_t* gh = a.hist + (long)blockIdx.x % kHistShards * kHistBins;
+      for (int i = tid; i < G * kHistBins; i += NT) {
+        const int j = i / kHistBins;
+        const uint32_t c = hl[i];
+        if (c && j < nq)
+          atomicAdd(gh + (long)(t0 + j) * kHistShards * kHistBins + (i % kHistBins), c);
+      }
+    }
+  }
+}
+
+template <int G, int D, bool FP8, bool DOTS>
+static void launch_stream(const StreamArgs& sa, dim3 grid, hipStream_t st) {
+  if (sa.a.scale_f16) hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, true>), grid, dim3(kSNW * 64), 0, st, sa);
+  else hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, false>), grid, dim3(kSNW * 64), 0, st, sa);
+}
+
+template <int D, bool FP8, bool DOTS>
+static void launch_stream_g(int G, const StreamArgs& sa, dim3 grid, hipStream_t st) {
+  if (G == 1) launch_stream<1, D, FP8, DOTS>(sa, grid, st);
+  else if (G == 2) launch_stream<2, D, FP8, DOTS>(sa, grid, st);
+  else launch_stream<4, D, FP8, DOTS>(sa, grid, st);
+}
+
 }  // namespace dsa
 
 using dsa_host::fail;
@@ -581,9 +951,31 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
   const long gy = (long)bt->num_seqs * a.ngrp;
   if (gy > 65535L) return fail(DSA_ERR_INVALID_ARG, "%s: too many token groups", fn);
-  const dim3 grid((unsigned)((bt->max_kv_len + dsa::kCK - 1) / dsa::kCK), (unsigned)gy);
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = code == DSA_FP8_E4M3;
+  if (a.ngrp == 1) {
+    // decode: the streaming kernel, spans (multiples of 256 keys) sized for about one
+    // workgroup per CU
+    const int gk = 32 * dsa::kSNW;
+    const long groups = (long)(bt->max_kv_len + gk - 1) / gk;
+    long sg = (groups * bt->num_seqs + 255) / 256;
+    const long sg_max = dsa::stream_scl(G) / G / gk;
+    if (sg < 1) sg = 1;
+    if (sg > sg_max) sg = sg_max;
+    dsa::StreamArgs sa{a, (int)(sg * gk)};
+    const dim3 grid((unsigned)((bt->max_kv_len + sa.span - 1) / sa.span), (unsigned)bt->num_seqs);
+    if (D == 128) {
+      if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_stream_g<128, false, true>(G, sa, grid, s); }
+      else if (fp8) dsa::launch_stream_g<128, true, false>(G, sa, grid, s);
+      else dsa::launch_stream_g<128, false, false>(G, sa, grid, s);
+    } else {
+      if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_stream_g<64, false, true>(G, sa, grid, s); }
+      else if (fp8) dsa::launch_stream_g<64, true, false>(G, sa, grid, s);
+      else dsa::launch_stream_g<64, false, false>(G, sa, grid, s);
+    }
+    return dsa_host::check_launch(fn);
+  }
+  const dim3 grid((unsigned)((bt->max_kv_len + dsa::kCK - 1) / dsa::kCK), (unsigned)gy);
   if (D == 128) {
     if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_g<2, 128, false, true>(G, a, grid, s); }
     else if (fp8) dsa::launch_g<2, 128, true, false>(G, a, grid, s);

@@ -37,6 +37,13 @@ constexpr int kCW = kChunk / 32;     // bitmap words per chunk
 constexpr int kMaxLen = 64 * kChunk; // longest row
 constexpr int kCap = 512;            // candidate slots per chunk
 constexpr int kLoadC = 4;            // candidate entries per finalize thread (first trip)
+constexpr int kRNT = 512;            // threads of a row workgroup (many-row batches)
+constexpr int kRNW = kRNT / 64;      // its waves
+constexpr int kRJ = 32;              // float4 slots per thread per segment
+constexpr int kQJ = 8;               // slots per ordered-prefix pass
+constexpr int kSeg = 4 * kRJ * kRNT; // scores per segment (65536)
+constexpr int kLc = 12288;           // compacted entries held in LDS
+constexpr int kRowMinT = 256;        // batches of at least this many rows take one workgroup per row
 
 // Workspace (zero-filled before the first call; every call leaves the histograms zero-filled
 // again, and the rest is written before it is read):
@@ -48,58 +55,8 @@ constexpr int kLoadC = 4;            // candidate entries per finalize thread (f
 struct TkArgs {
   const int32_t* q_pos; const float* scores; long ld; int k; int T; int nch;
   int32_t* idx; uint32_t* hist; uint32_t* bg; uint32_t* cnt; uint32_t* bits; uint64_t* slots;
+  int row_hist;                      // topk_row: hist holds the indexer's row histograms
 };
-
-// Inclusive prefix sum over the 64 lanes of a wave: four row shifts within each 16-lane row,
-// then the row broadcasts of lanes 15 and 31 (DPP, no LDS round trip).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
-  return v;
-}
-
-// Exclusive prefix sum over the NT threads of the block (one barrier); `total` gets the sum.
-// sh holds NT/64 words; consecutive uses of one sh must be separated by a barrier.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) sh[w] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const uint32_t x = sh[i];
-    before += i < w ? x : 0u;
-    tot += x;
-  }
-  total = tot;
-  return before + inc - v;
-}
-
-// The digit holding the need-th largest element of an LDS histogram over kBins digits:
-// res[0] = digit, res[1] = elements in larger digits.  Ends with a barrier.
-template <int NT>
-__device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* res) {
-  constexpr int PER = kBins / NT;
-  const int tid = threadIdx.x;
-  uint32_t loc[PER];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) { loc[j] = hist[kBins - 1 - (tid * PER + j)]; tot += loc[j]; }
-  uint32_t all;
-  uint32_t before = block_excl_scan<NT>(tot, sh, all);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (before < need && need <= before + loc[j]) { res[0] = kBins - 1 - (tid * PER + j); res[1] = before; }
-    before += loc[j];
-  }
-  __syncthreads();
-}
 
 // Keeps the loads issued above it in place: the compiler would otherwise sink loads that only
 // the non-returning path uses below an early-exit branch, which costs a second memory round
@@ -367,6 +324,305 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   }
 }
 
+// Ordered exclusive prefix over (slot j, thread) of per-thread counts c[j], j < NJ: the element
+// of slot j of thread t comes after every element of slots < j and after slot j of threads < t.
+// tbl: LDS [NJ * kRNW + 1]; ends with a barrier after which tbl may be reused.
+template <int NJ>
+__device__ __forceinline__ void prefix2d(const uint32_t (&c)[NJ], uint32_t (&off)[NJ],
+                                         uint32_t& total, uint32_t* tbl) {
+  static_assert(NJ * kRNW % 64 == 0 && NJ * kRNW <= 256, "one wave scans the table");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t inc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    inc[j] = wave_incl_scan(c[j]);
+    if (lane == 63) tbl[j * kRNW + w] = inc[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {                     // NJ x kRNW wave totals in (slot, wave) order
+    constexpr int Q = NJ * kRNW / 64;
+    uint32_t x[Q], sum = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) { x[q] = tbl[lane * Q + q]; sum += x[q]; }
+    const uint32_t incl = wave_incl_scan(sum);
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) { tbl[lane * Q + q] = run; run += x[q]; }
+    if (lane == 63) tbl[NJ * kRNW] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) off[j] = tbl[j * kRNW + w] + inc[j] - c[j];
+  total = tbl[NJ * kRNW];
+  __syncthreads();
+}
+
+// This thread's float4 slots of segment s (positions s * kSeg + 4 * (tid + kRNT * j) .. + 3);
+// addresses are clamped into the row's ld columns, positions past p are masked by the caller.
+__device__ __forceinline__ void load_seg(float4 (&v)[kRJ], const float* row, long ld, int s) {
+#pragma unroll
+  for (int j = 0; j < kRJ; ++j) {
+    const long e0 = min((long)s * kSeg + 4 * ((long)threadIdx.x + (long)kRNT * j), (ld & ~3L) - 4);
+    v[j] = *reinterpret_cast<const float4*>(row + e0);
+  }
+}
+
+__device__ __forceinline__ float f4get(const float4& v, int r) {
+  return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ void issue_fence_row() { asm volatile("" ::: "memory"); }
+
+// Many-row batches (a prefill chunk: thousands of rows): one workgroup per row finishes the
+// selection on its own, with no second launch.  One memory round trip brings the row histogram
+// and the row's first 65536 scores (registers); every key with digit >= b1 is compacted into
+// LDS in position order (an ordered prefix over (float4 slot, thread)); two more digits over the
+// candidates give K*; the selection is one ordered pass over the compacted list.  Rows with more
+// entries than LDS holds re-read the row for each pass.  On a decode batch of a few rows this
+// is slower than spreading each row over its chunks (one CU's ALUs order 65536 keys in ~15 us),
+// which is why it serves many-row batches only.
+__global__ void __launch_bounds__(kRNT) topk_row(TkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint64_t lst[kLc];       // compacted (key << 32 | pos)
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins];
+  __shared__ uint32_t tbl[kQJ * kRNW + 1];
+  __shared__ uint32_t sh[kRNT / 64];
+  __shared__ uint32_t res[2];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int k = a.k;
+  const float* row = a.scores + (long)t * a.ld;
+  // ---- one round trip: q_pos, the row histogram and the first segment
+  const int p = a.q_pos[t];
+  uint32_t hv[2] = {0u, 0u};
+  uint32_t hv2[2] = {0u, 0u};
+  {
+    // loaded unconditionally (the workspace rows are zero when the indexer did not fill them), so
+    // that every load of the round trip is issued before the first wait
+    const uint32_t* gh = a.hist + (long)t * kShards * kBins;
+#pragma unroll
+    for (int sd = 0; sd < kShards; ++sd) {
+      hv[0] += gh[sd * kBins + tid]; hv[1] += gh[sd * kBins + kRNT + tid];
+      hv2[0] += gh[sd * kBins + 2 * kRNT + tid]; hv2[1] += gh[sd * kBins + 3 * kRNT + tid];
+    }
+  }
+  float4 v[kRJ];
+  load_seg(v, row, a.ld, 0);
+  issue_fence_row();
+  int32_t* out = a.idx + (long)t * k;
+  if (p + 1 <= k) {                                  // a short row: everything, then -1
+    for (int j = tid; j < k; j += kRNT) out[j] = j <= p ? j : -1;
+    return;
+  }
+  const int L = p + 1;
+  const int nseg = (L + kSeg - 1) / kSeg;
+  // ---- the first digit: the indexer's histogram (cleared for the next call), or built here
+  if (a.row_hist) {
+    h[tid] = hv[0]; h[kRNT + tid] = hv[1]; h[2 * kRNT + tid] = hv2[0]; h[3 * kRNT + tid] = hv2[1];
+    uint32_t* gh = a.hist + (long)t * kShards * kBins;
+#pragma unroll
+    for (int sd = 0; sd < kShards; ++sd)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gh[sd * kBins + q * kRNT + tid] = 0u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q * kRNT + tid] = 0u;
+    __syncthreads();
+    // segment 0 from the registers, later segments through a small buffer (the registers keep
+    // segment 0 for the compaction)
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * (tid + kRNT * j) + r < L) atomicAdd(&h[order_key(f4get(v[j], r)) >> 21], 1u);
+    for (int s = 1; s < nseg; ++s)
+      for (int j0 = 0; j0 < kRJ; j0 += kQJ) {
+        float4 w[kQJ];
+#pragma unroll
+        for (int j = 0; j < kQJ; ++j) {
+          const long e0 = min((long)s * kSeg + 4 * ((long)tid + (long)kRNT * (j0 + j)), (a.ld & ~3L) - 4);
+          w[j] = *reinterpret_cast<const float4*>(row + e0);
+        }
+#pragma unroll
+        for (int j = 0; j < kQJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (s * kSeg + 4 * (tid + kRNT * (j0 + j)) + r < L)
+              atomicAdd(&h[order_key(f4get(w[j], r)) >> 21], 1u);
+      }
+  }
+  if (tid == 0) { res[0] = 0u; res[1] = 0u; }
+  __syncthreads();
+  find_digit_desc<kRNT>(h, (uint32_t)k, sh, res);
+  const uint32_t b1 = res[0];
+  const uint32_t need = (uint32_t)k - res[1];        // >= 1 keys of digit b1 are taken
+  // ---- keys with digit >= b1, compacted in position order
+  // (slots are position-major, so each group of kQJ slots is compacted on its own)
+  constexpr int HJ = kQJ;
+  uint32_t n_list = 0;
+  for (int s = 0; s < nseg; ++s) {
+    if (s > 0) load_seg(v, row, a.ld, s);
+#pragma unroll
+    for (int hh = 0; hh < kRJ / kQJ; ++hh) {
+      uint32_t c[HJ], off[HJ], tot;
+#pragma unroll
+      for (int jj = 0; jj < HJ; ++jj) {
+        const int j = hh * HJ + jj;
+        c[jj] = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = s * kSeg + 4 * (tid + kRNT * j) + r;
+          c[jj] += pos < L && (order_key(f4get(v[j], r)) >> 21) >= b1;
+        }
+      }
+      prefix2d<HJ>(c, off, tot, tbl);
+#pragma unroll
+      for (int jj = 0; jj < HJ; ++jj) {
+        const int j = hh * HJ + jj;
+        uint32_t o = n_list + off[jj];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = s * kSeg + 4 * (tid + kRNT * j) + r;
+          const uint32_t key = order_key(f4get(v[j], r));
+          if (pos < L && (key >> 21) >= b1) {
+            if (o < (uint32_t)kLc) lst[o] = ((uint64_t)key << 32) | (uint32_t)pos;
+            ++o;
+          }
+        }
+      }
+      n_list += tot;
+    }
+  }
+  __syncthreads();
+  const bool listed = n_list <= (uint32_t)kLc;
+  // every key of digit b1, from the list or (rows too long for it) from the scores
+  auto each_cand = [&](auto&& fn) {
+    if (listed) {
+      for (uint32_t f = tid; f < n_list; f += kRNT) {
+        const uint64_t e = lst[f];
+        const uint32_t key = (uint32_t)(e >> 32);
+        if ((key >> 21) == b1) fn(key);
+      }
+    } else {
+      for (int s = 0; s < nseg; ++s) {
+        load_seg(v, row, a.ld, s);
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t key = order_key(f4get(v[j], r));
+            if (s * kSeg + 4 * (tid + kRNT * j) + r < L && (key >> 21) == b1) fn(key);
+          }
+      }
+    }
+  };
+  // ---- two more digits: the exact k-th key K*
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h[q * kRNT + tid] = 0u;
+  if (tid == 0) { res[0] = 0u; res[1] = 0u; }
+  __syncthreads();
+  each_cand([&](uint32_t key) { atomicAdd(&h[(key >> 10) & 0x7FFu], 1u); });
+  __syncthreads();
+  find_digit_desc<kRNT>(h, need, sh, res);
+  const uint32_t b2 = res[0];
+  const uint32_t need2 = need - res[1];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h[q * kRNT + tid] = 0u;
+  if (tid == 0) { res[0] = 0u; res[1] = 0u; }
+  __syncthreads();
+  each_cand([&](uint32_t key) {
+    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h[key & 0x3FFu], 1u);
+  });
+  __syncthreads();
+  find_digit_desc<kRNT>(h, need2, sh, res);
+  const uint32_t kstar = (b1 << 21) | (b2 << 10) | res[0];
+  const uint32_t take_eq = need2 - res[1];          // >= 1 keys equal to K* are taken
+  // ---- the selection, in position order: keys above K*, and the first take_eq keys equal to K*
+  if (listed) {
+    constexpr int PER = (kLc + kRNT - 1) / kRNT;     // list entries per thread (a contiguous run)
+    const uint32_t e0 = (uint32_t)tid * PER;
+    uint32_t keys[PER];
+    uint32_t nt = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      keys[u] = e0 + u < n_list ? (uint32_t)(lst[e0 + u] >> 32) : 0u;
+      nt += e0 + u < n_list && keys[u] == kstar;
+    }
+    uint32_t tt;
+    uint32_t rank = block_excl_scan<kRNT>(nt, sh, tt);   // equal keys before this run
+    uint32_t nsel = 0, selm = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      bool sel = false;
+      if (e0 + u < n_list) {
+        if (keys[u] > kstar) sel = true;
+        else if (keys[u] == kstar) { sel = rank < take_eq; ++rank; }
+      }
+      selm |= (uint32_t)sel << u;
+      nsel += sel;
+    }
+    __syncthreads();
+    uint32_t st;
+    uint32_t o = block_excl_scan<kRNT>(nsel, sh, st);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if ((selm >> u) & 1u) {
+        if (o < (uint32_t)k) out[o] = (int32_t)(uint32_t)lst[e0 + u];
+        ++o;
+      }
+  } else {
+    uint32_t o_base = 0, t_base = 0;
+    for (int s = 0; s < nseg; ++s) {
+      load_seg(v, row, a.ld, s);
+#pragma unroll
+      for (int hh = 0; hh < kRJ / kQJ; ++hh) {
+        uint32_t c[HJ], off[HJ], tot;
+#pragma unroll
+        for (int jj = 0; jj < HJ; ++jj) {
+          const int j = hh * HJ + jj;
+          c[jj] = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            c[jj] += s * kSeg + 4 * (tid + kRNT * j) + r < L && order_key(f4get(v[j], r)) == kstar;
+        }
+        prefix2d<HJ>(c, off, tot, tbl);              // equal keys before each slot
+        uint32_t sc[HJ], soff[HJ], stot;
+#pragma unroll
+        for (int jj = 0; jj < HJ; ++jj) {
+          const int j = hh * HJ + jj;
+          sc[jj] = 0;
+          uint32_t rank = t_base + off[jj];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t key = order_key(f4get(v[j], r));
+            if (s * kSeg + 4 * (tid + kRNT * j) + r < L) {
+              if (key > kstar) ++sc[jj];
+              else if (key == kstar) { sc[jj] += rank < take_eq; ++rank; }
+            }
+          }
+        }
+        prefix2d<HJ>(sc, soff, stot, tbl);
+#pragma unroll
+        for (int jj = 0; jj < HJ; ++jj) {
+          const int j = hh * HJ + jj;
+          uint32_t o = o_base + soff[jj];
+          uint32_t rank = t_base + off[jj];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int pos = s * kSeg + 4 * (tid + kRNT * j) + r;
+            const uint32_t key = order_key(f4get(v[j], r));
+            if (pos < L) {
+              bool sel = key > kstar;
+              if (key == kstar) { sel = rank < take_eq; ++rank; }
+              if (sel) { if (o < (uint32_t)k) out[o] = pos; ++o; }
+            }
+          }
+        }
+        o_base += stot;
+        t_base += tot;
+      }
+    }
+  }
+}
+
 }  // namespace dsa
 
 using dsa_host::fail;
@@ -445,6 +701,11 @@ extern "C" dsa_status dsa_topk(const dsa_batch* bt, const float* scores, int64_t
   const dsa_status st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a);
   if (st != DSA_OK || bt->num_q == 0) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (a.T >= dsa::kRowMinT) {                            // the row workgroups build their histograms
+    a.row_hist = 0;
+    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, s, a);
+    return dsa_host::check_launch(fn);
+  }
   hipLaunchKernelGGL(dsa::topk_hist, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
   topk_tail(a, s);
   return dsa_host::check_launch(fn);
@@ -468,7 +729,12 @@ static dsa_status indexer_topk(const dsa_batch* bt, const dsa_paging* pg, int32_
   st = dsa_indexer_scores_hist(bt, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
                                k_scale, scores, ld, bt->num_q ? a.hist : nullptr, k, stream, fn, pg);
   if (st != DSA_OK || bt->num_q == 0) return st;
-  topk_tail(a, (hipStream_t)stream);
+  if (a.T >= dsa::kRowMinT) {
+    a.row_hist = 1;
+    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, (hipStream_t)stream, a);
+  } else {
+    topk_tail(a, (hipStream_t)stream);
+  }
   return dsa_host::check_launch(fn);
 }
 

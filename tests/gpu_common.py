@@ -152,6 +152,18 @@ def check_topk(gi: torch.Tensor, oi: np.ndarray, os_rows, q_pos, k: int) -> int:
     return diffs
 
 
+def topk_zeroed_bytes(T: int) -> int:
+    """Bytes of a top-k workspace that every call leaves zero: the row histograms (4 shards x
+    2048 bins per token) that the indexer accumulates for the top-k."""
+    return (T * 4 * 2048 * 4 + 255) // 256 * 256
+
+
+def check_zeroed_workspace(ws: torch.Tensor, T: int) -> None:
+    z = ws[:topk_zeroed_bytes(T)]
+    bad = int(torch.count_nonzero(z).item())
+    assert bad == 0, f"top-k workspace: {bad} non-zero bytes left in the row histograms"
+
+
 def sfa_errors(gout: torch.Tensor, oout: np.ndarray, tokens=None):
     g = gout.float().cpu().numpy().astype(np.float64)
     if tokens is not None:
@@ -181,6 +193,7 @@ def run_e2e(wl, token_subset=None, check_dots=False):
                      dtype=torch.uint8, device="cuda")
     sc, idx = g.indexer_topk(ws)
     _, idx_again = g.indexer_topk(ws)
+    check_zeroed_workspace(ws, wl.T)
     idx_sep = g.topk(g.scores())
     out = g.sfa(idx)
     torch.cuda.synchronize()

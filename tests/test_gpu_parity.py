@@ -121,6 +121,26 @@ def test_topk_exact_on_identical_scores(rng, kind):
     assert np.array_equal(idx, ref)
 
 
+def test_indexer_topk_all_ties_take_lowest_positions():
+    """Every score equal (zero head weights): every key of a row is in the threshold digit, so the
+    row workgroup's ordered list holds the whole row (9000 and 2100 keys) or overflows it (70000
+    keys, resolved by re-reading the row); the ties go to the lowest positions, exactly as the
+    standalone top-k, and the row histograms are left zero."""
+    from gpu_common import check_zeroed_workspace
+    sp = Spec("all_ties", 7210, [9000, 70000, 2100], [2, 1, 1], k=2048, Hq=16)
+    wl = make(sp)
+    wl.w[:] = 0
+    g = Gpu(wl)
+    ws = torch.zeros(dsa.dsa_topk_workspace_size(wl.T, g.batch.max_kv_len, 2048), dtype=torch.uint8,
+                     device="cuda")
+    log("case indexer + top-k, all ties")
+    _, idx = g.indexer_topk(ws)
+    check_zeroed_workspace(ws, wl.T)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, np.tile(np.arange(2048), (wl.T, 1)))
+    assert torch.equal(idx, g.topk(g.scores()))
+
+
 def test_topk_all_zero_weights_select_first_positions():
     sp = Spec("ties_w0", 7200, [9000, 3000], [1, 1], k=1024, Hq=16)
     wl = make(sp)
