@@ -266,6 +266,21 @@ dsa_status dsa_sparse_attn_merge(const dsa_batch* batch, int32_t Hq, int32_t k,
                                  const float* sink, void* out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc): dsa_sparse_attn_decode with the same arguments, results and errors except
+ * the workspace, which is a fixed scratch array of 12 MiB that the library holds on every GPU it
+ * runs on (from the first call on that GPU until the process ends).  Calls whose split partials
+ * (dsa_sparse_attn_workspace_size) exceed 12 MiB return DSA_ERR_UNSUPPORTED before any launch;
+ * decode batches of up to 32 query tokens at 128 heads and k <= 2048 fit.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (concurrent streams) race.  Nothing
+ * in the scratch needs clearing between calls.
+ */
+dsa_status dsa_sparse_attn_decode_noalloc(const dsa_batch* batch, int32_t Hq, const void* q,
+                                          const void* kv, int64_t kv_row_stride,
+                                          const int32_t* idx, int32_t k, const float* sink,
+                                          float scale, void* out, void* stream);
+
 /* ---------------------------------------------------------------- paged caches ----------- */
 /*
  * [LI] the Page Attention layout of the caches: a sequence's rows are stored in fixed-size

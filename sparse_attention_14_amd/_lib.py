@@ -73,6 +73,8 @@ SIGNATURES = {
     "dsa_sparse_attn_split": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
                                              ctypes.c_float, _P, _P, _SZ, _P]),
     "dsa_sparse_attn_merge": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "dsa_sparse_attn_decode_noalloc": (ctypes.c_int, [_BP, _I32, _P, _P, _I64, _P, _I32, _P,
+                                                      ctypes.c_float, _P, _P]),
     "dsa_indexer_scores_paged": (ctypes.c_int, [_BP, _PP, _I32, _I32, ctypes.c_int, ctypes.c_int,
                                                 _P, _P, _P, _P, _P, _P, _I64, _P]),
     "dsa_indexer_topk_paged": (ctypes.c_int, [_BP, _PP, _I32, _I32, ctypes.c_int, ctypes.c_int,

@@ -24,6 +24,8 @@
 // A split writes its own softmax average O / l in bf16 with its running max and sum (fp32)
 // when the selection is spread over several workgroups; the combine kernel merges them in fp32
 // with the sink.  With one split the main kernel applies the sink and writes bf16 directly.
+#include <mutex>
+
 #include "common.h"
 
 namespace dsa {
@@ -544,6 +546,35 @@ static SfaPlan plan(int T, int Hq, int k) {
 
 using dsa_host::fail;
 dsa_status dsa_check_batch(const dsa_batch* bt, const char* fn);
+
+// Fixed scratch for the split partials of dsa_sparse_attn_decode_noalloc (callers that cannot
+// allocate).  Each GPU holds its own copy until the process ends; host code uses the device
+// address resolved per device below, never this name.
+constexpr size_t kScratchBytes = (size_t)12 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+}  // namespace
+
+// The device address of `scratch` on the current device (resolved once per device).
+static dsa_status scratch_address(void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(DSA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
 dsa_status dsa_check_batch_paged(const dsa_batch* bt, const char* fn);
 dsa_status dsa_check_paging(const dsa_paging* pg, const dsa_batch* bt, double row_bytes,
                             const char* fn, int* bs_log2);
@@ -673,6 +704,37 @@ extern "C" dsa_status dsa_sparse_attn_merge(const dsa_batch* bt, int32_t Hq, int
   const dsa_status st = sfa_prepare(bt, Hq, out, out, dsa::kDqk, (const int32_t*)out, k, sink,
                                     1.f, out, ws, ws_bytes, fn, &a, &p);
   if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_merge(a, p, (hipStream_t)stream);
+  return dsa_host::check_launch(fn);
+}
+
+// dsa_sparse_attn_decode with the split partials in the library's fixed per-GPU scratch (no
+// workspace argument, no allocation).  Rejects calls whose partials exceed the scratch.
+extern "C" dsa_status dsa_sparse_attn_decode_noalloc(const dsa_batch* bt, int32_t Hq, const void* q,
+                                                     const void* kv, int64_t kv_row_stride,
+                                                     const int32_t* idx, int32_t k, const float* sink,
+                                                     float scale, void* out, void* stream) {
+  const char* fn = "dsa_sparse_attn_decode_noalloc";
+  if (!bt) return fail(DSA_ERR_INVALID_ARG, "%s: batch is NULL", fn);
+  if (bt->num_q > 0 && Hq > 0 && k > 0) {
+    const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
+    if (need > kScratchBytes)
+      return fail(DSA_ERR_UNSUPPORTED, "%s: split partials of %zu bytes exceed the fixed scratch of %zu bytes",
+                  fn, need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (bt->num_q > 0 && dsa_sparse_attn_workspace_size(bt->num_q, Hq, k) > 0) {
+    const dsa_status st = scratch_address(&ws, fn);
+    if (st != DSA_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
+                                    ws_bytes, fn, &a, &p);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  sfa_launch_split(a, p, (hipStream_t)stream);
   sfa_launch_merge(a, p, (hipStream_t)stream);
   return dsa_host::check_launch(fn);
 }

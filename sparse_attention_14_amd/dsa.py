@@ -257,7 +257,21 @@ def dsa_sparse_attn_decode(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx:
     return out
 
 
-def _sfa_args(batch: Batch, q, kv, idx, sink, out, ws):
+def dsa_sparse_attn_decode_noalloc(batch: Batch, q: torch.Tensor, kv: torch.Tensor,
+                                   idx: torch.Tensor, sink: Optional[torch.Tensor], scale: float,
+                                   out: torch.Tensor) -> torch.Tensor:
+    """dsa_sparse_attn_decode with the split partials in the library's fixed per-GPU scratch
+    (no workspace; `out` must be given, so nothing is allocated)."""
+    _need(out, "out", torch.bfloat16)
+    Hq, k, out, _ = _sfa_args(batch, q, kv, idx, sink, out, None, want_ws=False)
+    b = batch.c()
+    check("dsa_sparse_attn_decode_noalloc", lib.dsa_sparse_attn_decode_noalloc(
+        ctypes.byref(b), Hq, _ptr(q), _ptr(kv), kv.stride(0), _ptr(idx), k, _ptr(sink),
+        ctypes.c_float(scale), _ptr(out), _stream()))
+    return out
+
+
+def _sfa_args(batch: Batch, q, kv, idx, sink, out, ws, want_ws: bool = True):
     T = batch.num_q
     if q.dim() != 3:
         raise ValueError("q must be [T, Hq, 576]")
@@ -274,7 +288,7 @@ def _sfa_args(batch: Batch, q, kv, idx, sink, out, ws):
         out = torch.empty((T, Hq, D_V), dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, (T, Hq, D_V))
     need = dsa_sparse_attn_workspace_size(T, Hq, k)
-    if ws is None and need:
+    if want_ws and ws is None and need:
         ws = _workspace(need, q.device)
     return Hq, k, out, ws
 
