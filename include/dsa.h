@@ -146,6 +146,25 @@ dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,
                                 const int8_t* q_codes, const int8_t* k_cache,
                                 int32_t* dots, int64_t ld, void* stream);
 
+/*
+ * Test hook for the choice of the fp8 indexer contraction ([PRO] quantization strategy: fp8
+ * query and fp8 key cache).  c[i, j] = sum_d a[i, d] * b[j, d] over e4m3 codes, in fp32, on:
+ *   DSA_CONTRACT_BF16     codes widened to bf16 (exact), v_mfma_f32_32x32x16_bf16 -- the
+ *                         contraction dsa_indexer_scores uses for e4m3 codes;
+ *   DSA_CONTRACT_FP8_K64  v_mfma_scale_f32_32x32x64_f8f6f4 on the codes, unit scales;
+ *   DSA_CONTRACT_FP8_K16  v_mfma_f32_32x32x16_fp8_fp8 on the codes.
+ *   a  device [m, d] e4m3 codes    b  device [n, d] e4m3 codes    c  device [m, n] fp32
+ * m and n multiples of 32 (m < 2^21), d a multiple of 64 in [64, 4096]; a and b 16-byte
+ * aligned.  Every path forms the same exact products and differs only in how it sums them.
+ */
+typedef enum dsa_contraction {
+  DSA_CONTRACT_BF16 = 0,
+  DSA_CONTRACT_FP8_K64 = 1,
+  DSA_CONTRACT_FP8_K16 = 2
+} dsa_contraction;
+dsa_status dsa_e4m3_dots(const uint8_t* a, int32_t m, const uint8_t* b, int32_t n, int32_t d,
+                         int32_t contraction, float* c, void* stream);
+
 /* ---------------------------------------------------------------- upstream projections ---- */
 /*
  * [PRO] Indexer Prolog formulas, the parts before RoPE: the indexer query's W8A8 linear

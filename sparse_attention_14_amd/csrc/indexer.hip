@@ -40,9 +40,11 @@ constexpr int kBlk = 32;     // keys per MFMA column block
 //  fp8 : the bytes are widened to bf16 in registers (every e4m3 value is exactly a bf16;
 //        v_cvt_scalef32_pk_bf16_fp8 with unit scale converts two codes per instruction) and
 //        contracted on v_mfma_f32_32x32x16_bf16 (k = 16): products are exact in fp32 and the
-//        sums carry fp32 rounding only.  The fp8 MFMA itself accumulates with a narrower
-//        internal adder (about 2e-5 relative error on these dots), too coarse for the top-k
-//        near-tie tolerance, so it is not used here.
+//        sums carry fp32 rounding only (measured: within 1e-7 of the row's largest dot, under
+//        one fp32 ulp of sum |a b|).  Both fp8 MFMAs (32x32x64 f8f6f4 and 32x32x16 fp8) sum with
+//        a narrower internal adder: up to 2.7e-5 of the row's largest dot on the same codes
+//        (about 320 ulps), above the 1e-6 a head dot may carry under the top-k near-tie rule,
+//        so they are not used here (dsa_e4m3_dots runs all three).
 template <bool FP8, int D>
 struct KFrag;
 template <int D>
@@ -1024,4 +1026,72 @@ extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, in
                                            int32_t* dots, int64_t ld, void* stream) {
   return indexer_common(batch, H, D, DSA_I8, DSA_F32, q_codes, nullptr, nullptr, k_cache, nullptr,
                         nullptr, dots, true, ld, nullptr, 0, stream, "dsa_indexer_dots_i32");
+}
+
+// ---------------------------------------------------------------------------------------------
+// Test hook for the choice of the fp8 indexer contraction: C = A B^T over e4m3 codes on one of
+// three matrix-core paths.  One wave per 32 x 32 block of C; per 16-deep step the lane holding
+// row (or column) l % 32 supplies the 8 codes at depth 8 (l / 32) of that step, for A and B
+// alike, so every path forms the same products and differs only in how it sums them.
+namespace dsa {
+__global__ void __launch_bounds__(64) e4m3_dots_kernel(const uint8_t* A, const uint8_t* B, int n,
+                                                       int d, int path, float* C) {
+  const int lane = threadIdx.x;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const uint8_t* ar = A + (long)(i0 + (lane & 31)) * d + 8 * (lane >> 5);
+  const uint8_t* br = B + (long)(j0 + (lane & 31)) * d + 8 * (lane >> 5);
+  v16f acc = {};
+  if (path == DSA_CONTRACT_FP8_K64) {
+    // v_mfma_scale_f32_32x32x64_f8f6f4, both operands e4m3 (format 0), unit E8M0 scales (127)
+    for (int k0 = 0; k0 < d; k0 += 64) {
+      v8i a8, b8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint2 av = *reinterpret_cast<const uint2*>(ar + k0 + 16 * s);
+        const uint2 bv = *reinterpret_cast<const uint2*>(br + k0 + 16 * s);
+        a8[2 * s] = (int)av.x; a8[2 * s + 1] = (int)av.y;
+        b8[2 * s] = (int)bv.x; b8[2 * s + 1] = (int)bv.y;
+      }
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc, 0, 0, 0, 127, 0, 127);
+    }
+  } else if (path == DSA_CONTRACT_FP8_K16) {
+    for (int k0 = 0; k0 < d; k0 += 16) {
+      const long av = *reinterpret_cast<const long*>(ar + k0);
+      const long bv = *reinterpret_cast<const long*>(br + k0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av, bv, acc, 0, 0, 0);
+    }
+  } else {
+    // the fp8 indexer's own contraction: codes widened to bf16, v_mfma_f32_32x32x16_bf16
+    for (int k0 = 0; k0 < d; k0 += 16) {
+      const uint2 av = *reinterpret_cast<const uint2*>(ar + k0);
+      const uint2 bv = *reinterpret_cast<const uint2*>(br + k0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16<0>((int)av.x, (int)av.y),
+                                                    fp8x8_to_bf16<0>((int)bv.x, (int)bv.y), acc, 0, 0, 0);
+    }
+  }
+  // 32 x 32 accumulator: register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    C[(long)i * n + j0 + (lane & 31)] = acc[r];
+  }
+}
+}  // namespace dsa
+
+extern "C" dsa_status dsa_e4m3_dots(const uint8_t* a, int32_t m, const uint8_t* b, int32_t n,
+                                    int32_t d, int32_t contraction, float* c, void* stream) {
+  const char* fn = "dsa_e4m3_dots";
+  if (contraction != DSA_CONTRACT_BF16 && contraction != DSA_CONTRACT_FP8_K64 &&
+      contraction != DSA_CONTRACT_FP8_K16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: unknown contraction %d", fn, contraction);
+  if (m < 0 || n < 0 || m % 32 || n % 32) return fail(DSA_ERR_INVALID_ARG, "%s: m and n must be multiples of 32", fn);
+  if (d <= 0 || d % 64 || d > 4096) return fail(DSA_ERR_INVALID_ARG, "%s: d must be a multiple of 64 in [64, 4096]", fn);
+  if (m == 0 || n == 0) return DSA_OK;
+  if (!a || !b || !c) return fail(DSA_ERR_INVALID_ARG, "%s: a data pointer is NULL", fn);
+  if (((uintptr_t)a | (uintptr_t)b) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: a and b must be 16-byte aligned", fn);
+  if ((uintptr_t)c & 3) return fail(DSA_ERR_INVALID_ARG, "%s: c must be 4-byte aligned", fn);
+  if ((long)m / 32 > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: m must be < 2097152", fn);
+  hipLaunchKernelGGL(dsa::e4m3_dots_kernel, dim3((unsigned)(n / 32), (unsigned)(m / 32)), dim3(64), 0,
+                     (hipStream_t)stream, a, b, n, d, (int)contraction, c);
+  return dsa_host::check_launch(fn);
 }

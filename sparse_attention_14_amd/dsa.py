@@ -181,6 +181,22 @@ def dsa_indexer_dots_i32(batch: Batch, H: int, D: int, q_codes, k_cache,
     return dots
 
 
+CONTRACTIONS = {"bf16": 0, "fp8_k64": 1, "fp8_k16": 2}
+
+
+def dsa_e4m3_dots(a, b, contraction: str) -> torch.Tensor:
+    """fp32 C = A B^T over e4m3 codes (uint8 [m, d] and [n, d]) on one matrix-core path:
+    "bf16" (the fp8 indexer's widening), "fp8_k64" or "fp8_k16" (test hook)."""
+    _need(a, "a", torch.uint8)
+    _need(b, "b", torch.uint8)
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("a and b must be [m, d] and [n, d]")
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.float32, device=a.device)
+    check("dsa_e4m3_dots", lib.dsa_e4m3_dots(_ptr(a), a.shape[0], _ptr(b), b.shape[0], a.shape[1],
+                                             CONTRACTIONS[contraction], _ptr(c), _stream()))
+    return c
+
+
 def dsa_topk_workspace_size(num_q: int, max_kv_len: int, k: int) -> int:
     return int(lib.dsa_topk_workspace_size(num_q, max_kv_len, k))
 

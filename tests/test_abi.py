@@ -94,6 +94,12 @@ def test_validation_errors_before_any_device_call():
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, P, P, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
     cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, None, None, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
+    # fp8 contraction hook: unknown path, ragged sizes, bad depth, misaligned operand; empty is a no-op
+    assert lib.dsa_e4m3_dots(P, 32, P, 32, 128, 3, P, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_e4m3_dots(P, 33, P, 32, 128, 0, P, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_e4m3_dots(P, 32, P, 32, 96, 1, P, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_e4m3_dots(ctypes.c_void_p(0x1008), 32, P, 32, 128, 2, P, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_e4m3_dots(None, 0, None, 32, 128, 0, None, None) == L.DSA_OK
 
 
 def test_empty_batches_are_noops_without_device():
