@@ -469,11 +469,13 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
 // Merge split partials: with a_s = O_s / l_s (stored bf16), m_s, l_s (fp32) per split,
 //   o = sum_s 2^(m_s - M) l_s a_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)),  M = max(m_s, sink).
 // One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64), the wave reduces
-// them with shuffles, then each lane accumulates 8 value dims over the splits.
+// them with shuffles, then each lane accumulates 8 value dims over the splits.  Workgroups are
+// ordered like the split kernel's (xcd_remap over token-major ids), so a token's partials are
+// read on the XCD whose L2 received them.
 __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   constexpr int kPre = 8;                              // splits whose partials load up front
   const int lane = threadIdx.x & 63;
-  const int th = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int th = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
   const int t = th / a.Hq, h = th % a.Hq;
   const u16* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
