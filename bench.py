@@ -174,6 +174,15 @@ def main():
                                rope_offset=cfg.rope_offset, rope_interleaved=cfg.rope_interleaved,
                                hadamard=cfg.hadamard)
 
+    def st_prolog_indexer_topk(s):
+        dsa.dsa_indexer_prolog_topk(batch, H, D, cfg.code, cfg.scale_dt, q_in=s.q_in, k_in=s.k_in,
+                                    w=s.w, q_codes=s.buf.q_codes, q_scale=s.buf.q_scale,
+                                    k_cache=s.k_cache, k_scale=s.k_scale, k=k, q_cos=d0["q_cos"],
+                                    q_sin=d0["q_sin"], rope_dim=cfg.rope_dim,
+                                    rope_offset=cfg.rope_offset,
+                                    rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard,
+                                    scores=s.buf.scores, idx=s.buf.idx, ws=s.buf.ws_topk)
+
     def st_indexer(s):
         dsa.dsa_indexer_scores(batch, H, D, cfg.code, cfg.scale_dt, s.buf.q_codes, s.buf.q_scale,
                                s.w, s.k_cache, s.k_scale, scores=s.buf.scores)
@@ -304,7 +313,16 @@ def main():
         "paged calls differ from flat"
 
     # per-stage / per-kernel timing: R launches of one stage per graph replay
+    from sparse_attention_14_amd._lib import DSA_ERR_UNSUPPORTED, DsaError
+    try:                                   # the fused prolog serves decode-shaped batches only
+        st_prolog_indexer_topk(sets[0])
+        fused_stage = {"prolog_indexer_topk": st_prolog_indexer_topk}
+    except DsaError as e:
+        if e.status != DSA_ERR_UNSUPPORTED:
+            raise
+        fused_stage = {}
     stages = {"prolog": st_prolog, "indexer": st_indexer, "indexer_topk": st_indexer_topk,
+              **fused_stage,
               "sfa": st_sfa, "sfa_split": st_sfa_split, "sfa_merge": st_sfa_merge,
               "indexer_topk_paged": st_indexer_topk_paged, "sfa_paged": st_sfa_paged}
     stage_us = {}

@@ -138,6 +138,32 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, int32_t H, int32_t D,
                               float* scores, int64_t ld, void* stream);
 
 /*
+ * The indexer half of a step in one call ([DIA] "Deepseek Indexer Attention": the indexer
+ * prolog, the Lightning Indexer and its TopK run back to back).  The result equals
+ *   dsa_indexer_prolog(cfg, T, q_in, q_cos, q_sin, q_codes, q_scale,
+ *                      T, k_in, q_cos, q_sin, k_slot, k_cache, k_scale)
+ *   dsa_indexer_topk(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes,
+ *                    q_scale, w, k_cache, k_scale, k, scores, ld, idx, ws, ws_bytes)
+ * with k_slot[t] = kv_start[q_seq[t]] + q_pos[t]: row t of k_in (device [T, D] in_dtype) is the
+ * key of token t at its own position, rotated with the token's own table (q_cos/q_sin row t).
+ * q_codes / q_scale are outputs here (the quantized query, as dsa_indexer_prolog writes it).
+ * Schedule (chosen from the shapes; the results are identical): for decode batches with few
+ * key spans per sequence (at most 4 query tokens per sequence, at most 16 spans of the
+ * streaming indexer, rope_dim 0 or rope_offset % 8 == 0 and rope_dim % 16 == 0, the group's
+ * raw query rows within 64 KiB at D = 128 / 80 KiB at D = 64) the prolog runs inside the
+ * indexer kernel -- one launch fewer; otherwise as a launch of its own before it.  The
+ * environment variable DSA_PROLOG_SCHEDULE=fused|separate overrides the choice where the form
+ * is legal (testing).  (H, D) as for dsa_indexer_scores; flat caches only; q_in, k_in,
+ * q_codes, q_scale and w 16-byte aligned.
+ */
+dsa_status dsa_indexer_prolog_topk(const dsa_prolog_cfg* cfg, const dsa_batch* batch,
+                                   const void* q_in, const float* q_cos, const float* q_sin,
+                                   const void* k_in, const void* w, void* q_codes, void* q_scale,
+                                   void* k_cache, void* k_scale, int32_t k, float* scores,
+                                   int64_t ld, int32_t* idx, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
  * Test hook for the bit-exactness rule: the same int8 MFMA contraction as
  * dsa_indexer_scores, writing the raw int32 dot products dots[t, h, s] (device
  * [T, H, ld] int32, s = 0 .. p_t) instead of the weighted scores.  int8 codes only.

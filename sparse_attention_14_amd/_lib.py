@@ -64,6 +64,8 @@ SIGNATURES = {
                                           _P, _P, _P, _I64, _P]),
     "dsa_indexer_dots_i32": (ctypes.c_int, [_BP, _I32, _I32, _P, _P, _P, _I64, _P]),
     "dsa_e4m3_dots": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _I32, _P, _P]),
+    "dsa_indexer_prolog_topk": (ctypes.c_int, [ctypes.POINTER(DsaPrologCfg), _BP, _P, _P, _P, _P, _P,
+                                               _P, _P, _P, _P, _I32, _P, _I64, _P, _P, _SZ, _P]),
     "dsa_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_topk": (ctypes.c_int, [_BP, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "dsa_indexer_topk": (ctypes.c_int, [_BP, _I32, _I32, ctypes.c_int, ctypes.c_int, _P, _P, _P,

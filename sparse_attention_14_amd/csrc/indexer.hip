@@ -18,6 +18,9 @@
 // MFMA k-permutation: the contraction runs over all D dims, so A and B only need the same
 // (lane, byte) -> d assignment.  Lane half hv = lane/32 owns dims [hv*D/2, hv*D/2 + D/2) of
 // both the query row and the key row, so each lane reads D/2 contiguous bytes of its key row.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 
 namespace dsa {
@@ -503,6 +506,131 @@ static void launch_g(int G, const IdxArgs& a, dim3 grid, hipStream_t st) {
 
 
 // ---------------------------------------------------------------------------------------------
+// Prolog inside the streaming kernel (dsa_indexer_prolog_topk).  [PRO] "Indexer Prolog"
+// (jsqmd.com/news/787325): the query and the new cache key are quantized per token-head after
+// Hadamard(RoPE(.)); [AQ] "Activation Quantization" (mooersco.com/news/996258, section 4, steps
+// 1-3): fp32 amax, scale = amax / qmax, rne(clamp(x / scale)).
+//
+// One row per D/8 lanes, 8 consecutive elements per lane (element i = 8 li + e), read from LDS.
+// RoPE and the Hadamard run in fp64 (products of fp32 values are exact there; one rounding to fp32
+// at the end), the quantizer in fp32.  The quotient x / scale is formed as
+// fp32(fp64(x) * fp64(1 / scale)): the two fp64 roundings stay within 2^-51 relative, and the
+// quotient of two fp32 values is never within 2^-49 (relative) of an fp32 rounding midpoint, so
+// the result is the correctly rounded fp32 division -- the same codes as dsa_indexer_prolog.
+struct ProArgs {
+  const void* q_in; const void* k_in; const float* cs; const float* sn;   // tables [T][rope_dim/2]
+  uint8_t* q_codes; void* q_scale; uint8_t* k_cache; void* k_scale;
+  int in_bf16, rope_dim, rope_offset, rope_interleaved, hadamard, round_scale;
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ uint2 pro_quant8(const ProArgs& p, const unsigned char* raw,
+                                            const float* cs, const float* sn, float& scale) {
+  constexpr int LPR = D / 8;                               // lanes per row
+  const int lane = threadIdx.x & 63, li = lane % LPR;
+  float f[8];
+  if (p.in_bf16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(raw + li * 16);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_to_f32((u16)(wv[e] & 0xFFFFu));
+      f[2 * e + 1] = bf16_to_f32((u16)(wv[e] >> 16));
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(raw + li * 32);
+    const float4 b = *reinterpret_cast<const float4*>(raw + li * 32 + 16);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  if (p.rope_dim > 0 || p.hadamard) {
+    double x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (double)f[e];
+    if (p.rope_dim > 0) {
+      // partner of element i: i ^ 1 (interleaved, same lane) or i +- rope_dim / 2 (lane +- half / 8;
+      // the host requires rope_offset % 8 == 0 and rope_dim % 16 == 0 for this form)
+      const int half = p.rope_dim >> 1;
+      const int rel0 = li * 8 - p.rope_offset;
+      const bool lane_in = rel0 >= 0 && rel0 < p.rope_dim;
+      double pv[8];
+      if (p.rope_interleaved) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = x[e ^ 1];
+      } else {
+        const int src = lane_in ? lane + (rel0 < half ? half / 8 : -(half / 8)) : lane;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __shfl(x[e], src, kWave);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rel = rel0 + e;
+        if (rel >= 0 && rel < p.rope_dim) {
+          bool first;
+          int pair;
+          if (p.rope_interleaved) { first = (rel & 1) == 0; pair = rel >> 1; }
+          else { first = rel < half; pair = first ? rel : rel - half; }
+          const double c = (double)cs[pair], sn_ = (double)sn[pair];
+          // first of the pair: x1 c - x2 s ; second: x2 c + x1 s
+          x[e] = first ? x[e] * c - pv[e] * sn_ : x[e] * c + pv[e] * sn_;
+        }
+      }
+    }
+    if (p.hadamard) {
+      // natural (Sylvester) order: for stride h, (a, b) -> (a + b, a - b), a = the element whose
+      // index has bit h clear; strides 1, 2, 4 inside the lane, 8 .. D/2 across lanes
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((e & h) == 0) {
+            const double u = x[e], v = x[e + h];
+            x[e] = u + v; x[e + h] = u - v;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) {
+        const bool hi = (li & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double o = __shfl_xor(x[e], m, kWave);
+          x[e] = hi ? o - x[e] : x[e] + o;
+        }
+      }
+      const double norm = D == 128 ? 0.088388347648318440550 : 0.125;   // 1/sqrt(128), 1/sqrt(64)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= norm;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  const float qmax = FP8 ? 448.0f : 127.0f;
+  float s = amax / qmax;                                   // IEEE-rounded division
+  if (p.round_scale && s > 0.f) {
+    int ex;
+    const float m = frexpf(s, &ex);                        // s = m * 2^ex, m in [0.5, 1)
+    s = m == 0.5f ? s : ldexpf(1.0f, ex);
+  }
+  const double rs = s > 0.f ? 1.0 / (double)s : 0.0;
+  uint32_t code[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float y = s > 0.f ? (float)((double)f[e] * rs) : 0.f;
+    y = fminf(fmaxf(y, -qmax), qmax);
+    if constexpr (FP8) code[e] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
+    else code[e] = (uint32_t)(uint8_t)(int8_t)__float2int_rn(y);
+  }
+  scale = s;
+  return uint2{code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+               code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24};
+}
+
+// ---------------------------------------------------------------------------------------------
 // Streaming decode kernel (at most four query tokens per sequence).
 //
 // A workgroup of eight waves owns one sequence and a long span of its keys (SPAN keys, chosen on
@@ -565,9 +693,24 @@ __device__ __forceinline__ float add_half_swap(float v) {
 struct StreamArgs {
   IdxArgs a;
   int span;              // keys per workgroup (a multiple of 32 * kSNW)
+  ProArgs pro;           // PRO: the prolog's inputs and outputs
 };
 
-template <int G, int D, bool FP8, bool DOTS, bool SF16>
+// PRO (dsa_indexer_prolog_topk): the workgroup quantizes its group's query rows itself instead of
+// loading codes.  Their raw rows (and the rotary tables, and the raw new-key rows of the group)
+// move into LDS by direct loads -- into the ring slots 1 .. NB-1 of every wave, free until the
+// stream's second block is issued -- together with the stream's first block; every wave then
+// quantizes rows (one per D/8 lanes) into the query-code region, the last wave also the group's
+// new key rows whose positions fall in this span.  The wave that consumes the block holding such
+// a key copies its fresh codes over the row the stream read, the final pass uses its fresh scale,
+// and the workgroup writes the new key rows (and, workgroup 0 of the sequence, the query codes
+// and scales) at its end.
+template <int G, int D> struct ProStage {
+  static constexpr int SRB = (SShape<G, D>::NB - 1) * SShape<G, D>::BB;   // staging bytes per wave
+  static constexpr int CAP = kSNW * SRB;                                   // raw query bytes that fit
+};
+
+template <int G, int D, bool FP8, bool DOTS, bool SF16, bool PRO>
 __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa) {
   typedef SShape<G, D> S;
   constexpr int NT = kSNW * 64;
@@ -581,6 +724,12 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
   __shared__ __attribute__((aligned(16))) uint32_t sraw[G * S::HT * (SF16 ? 1 : 2) / 2 > 64 ? G * S::HT * (SF16 ? 1 : 2) / 2 : 64];
   __shared__ __attribute__((aligned(16))) float wqt[G][S::HT];
   __shared__ int sbt[S::SCL / G / 16 + 1];                    // paged: the span's block entries
+  constexpr int PG = PRO ? G : 1;
+  __shared__ __attribute__((aligned(16))) float qsc[PG][PRO ? S::HT : 1];        // query scales
+  __shared__ __attribute__((aligned(16))) unsigned char newk[PG][PRO ? D : 16];  // new key codes
+  __shared__ float newks[PG];                                                    // ... and scales
+  __shared__ __attribute__((aligned(16))) float ptab[PRO ? 2 * G * 64 : 4];      // cos, sin rows
+  __shared__ __attribute__((aligned(16))) unsigned char nkraw[PRO ? G * D * 4 : 16];   // raw new keys
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hv = lane >> 5, col = lane & 31;
@@ -647,15 +796,56 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
 
   // ---- DMA: query codes, head weights and query scales, then this wave's first NB - 1 blocks
   const unsigned q_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)qsm;
+  const unsigned ring_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  // PRO: does a new key of the group fall in this span?
+  bool has_new = false;
+#pragma unroll
+  for (int j = 0; j < G; ++j) has_new |= j < nq && pg[j] >= span0 && pg[j] < span0 + nkeys;
+  const int insz = sa.pro.in_bf16 ? 2 : 4;
+  const int rhalf = sa.pro.rope_dim >> 1;
   {
-    const uint8_t* qsrc = uniform_ptr(a.q_codes + (long)t0 * H * D);
-    const int qbytes = nq * H * D;                             // tokens past nq: clamped copies
-    if constexpr (S::QB >= 1024) {
-      for (int j = wave; j < S::QB / 1024; j += kSNW)
-        dma16(qsrc, (uint32_t)min(j * 1024 + lane * 16, qbytes - 16), q_base + j * 1024);
+    if constexpr (!PRO) {
+      const uint8_t* qsrc = uniform_ptr(a.q_codes + (long)t0 * H * D);
+      const int qbytes = nq * H * D;                             // tokens past nq: clamped copies
+      if constexpr (S::QB >= 1024) {
+        for (int j = wave; j < S::QB / 1024; j += kSNW)
+          dma16(qsrc, (uint32_t)min(j * 1024 + lane * 16, qbytes - 16), q_base + j * 1024);
+      } else {
+        for (int j = wave; j < (S::QB + 255) / 256; j += kSNW)
+          dma4(qsrc, (uint32_t)min(j * 256 + lane * 4, qbytes - 4), q_base + j * 256);
+      }
     } else {
-      for (int j = wave; j < (S::QB + 255) / 256; j += kSNW)
-        dma4(qsrc, (uint32_t)min(j * 256 + lane * 4, qbytes - 4), q_base + j * 256);
+      // raw query rows -> staging: byte o at wave (o / SRB)'s slots 1 .. NB-1, offset o % SRB
+      typedef ProStage<G, D> P;
+      const unsigned char* rsrc = uniform_ptr((const unsigned char*)sa.pro.q_in + (long)t0 * H * D * insz);
+      const int rbytes = nq * H * D * insz;                      // <= P::CAP (host check)
+      for (int j = wave; j * 1024 < rbytes; j += kSNW)
+        dma16(rsrc, (uint32_t)min(j * 1024 + lane * 16, rbytes - 16),
+              ring_base + (unsigned)((j * 1024 / P::SRB) * (S::NB * S::BB) + S::BB + (j * 1024) % P::SRB));
+      if (wave == kSNW - 2) {
+        const unsigned tab_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)ptab;
+        if (rhalf > 0) {
+          const int tbytes = nq * rhalf * 4;
+          const unsigned char* csrc = uniform_ptr((const unsigned char*)sa.pro.cs + (long)t0 * rhalf * 4);
+          const unsigned char* ssrc = uniform_ptr((const unsigned char*)sa.pro.sn + (long)t0 * rhalf * 4);
+          for (int j = 0; j * 256 < tbytes; ++j) {
+            dma4(csrc, (uint32_t)min(j * 256 + lane * 4, tbytes - 4), tab_base + j * 256);
+            dma4(ssrc, (uint32_t)min(j * 256 + lane * 4, tbytes - 4), tab_base + G * 64 * 4 + j * 256);
+          }
+        }
+        if (has_new) {
+          const int kbytes = nq * D * insz;
+          const unsigned char* ksrc = uniform_ptr((const unsigned char*)sa.pro.k_in + (long)t0 * D * insz);
+          const unsigned nk_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)nkraw;
+          if (kbytes >= 1024) {
+            for (int j = 0; j * 1024 < kbytes; ++j)
+              dma16(ksrc, (uint32_t)min(j * 1024 + lane * 16, kbytes - 16), nk_base + j * 1024);
+          } else {
+            for (int j = 0; j * 256 < kbytes; ++j)
+              dma4(ksrc, (uint32_t)min(j * 256 + lane * 4, kbytes - 4), nk_base + j * 256);
+          }
+        }
+      }
     }
     if constexpr (!DOTS) {
       if (wave == kSNW - 1) {
@@ -664,6 +854,8 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
         for (int j = 0; j < (G * S::HT * 2 + 255) / 256; ++j)
           dma4(wsrc, (uint32_t)min(j * 256 + lane * 4, wbytes - 4),
                (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)wraw + j * 256);
+      }
+      if (wave == kSNW - 1 && !PRO) {
         const int sb = SF16 ? 2 : 4;
         const int sbytes = nq * H * sb;
         const unsigned char* ssrc = uniform_ptr((const unsigned char*)a.q_scale + (long)t0 * H * sb);
@@ -697,7 +889,45 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
       }
     }
   };
-  for (int i = 0; i < S::NB - 1 && i < nbw; ++i) issue_block(i);
+  if constexpr (!PRO) {
+    for (int i = 0; i < S::NB - 1 && i < nbw; ++i) issue_block(i);
+  } else {
+    // the first block, then the prolog while it is in flight
+    if (nbw > 0) issue_block(0);
+    wait_blocks_after<S::NPB>(nbw > 0 ? 1 : 0);               // raw rows, tables, weights landed
+    idx_lds_barrier();
+    typedef ProStage<G, D> P;
+    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    const int li = lane % LPR, rp = lane / LPR;
+    const int R = nq * H;
+    for (int ps = wave; ps * RPW < R; ps += kSNW) {          // wave-uniform bound
+      const int r = min(ps * RPW + rp, R - 1);
+      const int j = r / H, h = r % H;
+      const int o = r * D * insz;
+      float sc;
+      const uint2 c = pro_quant8<D, FP8>(sa.pro, ring + (o / P::SRB) * (S::NB * S::BB) + S::BB + o % P::SRB,
+                                         ptab + j * rhalf, ptab + G * 64 + j * rhalf, sc);
+      if (ps * RPW + rp < R) {
+        *reinterpret_cast<uint2*>(qsm + (j * S::HT + h) * D + li * 8) = c;
+        if (li == 0) qsc[j][h] = SF16 ? f16_bits_to_f32(f32_to_f16_bits(sc)) : sc;
+      }
+    }
+    if (wave == kSNW - 1 && has_new) {
+      const int j = min(rp, nq - 1);
+      float sc;
+      const uint2 c = pro_quant8<D, FP8>(sa.pro, nkraw + j * D * insz, ptab + j * rhalf,
+                                         ptab + G * 64 + j * rhalf, sc);
+      int pj = pg[0];
+#pragma unroll
+      for (int jj = 1; jj < G; ++jj) if (jj == j) pj = pg[jj];
+      if (rp < nq && pj >= span0 && pj < span0 + nkeys) {
+        *reinterpret_cast<uint2*>(&newk[j][li * 8]) = c;
+        if (li == 0) newks[j] = SF16 ? f16_bits_to_f32(f32_to_f16_bits(sc)) : sc;
+      }
+    }
+    idx_lds_barrier();                                         // codes visible; staging free
+    for (int i = 1; i < S::NB - 1 && i < nbw; ++i) issue_block(i);
+  }
 
   // ---- staging: wait for the query, weights and scales (issued before the blocks), build
   // w * q_scale, then move this wave's operands into registers
@@ -708,8 +938,9 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
       const int j = tid / S::HT, h = tid % S::HT;
       const int jj = min(j, nq - 1);
       const u16 wv = ((const u16*)wraw)[jj * H + h];
-      const float qsv = SF16 ? f16_bits_to_f32(((const u16*)sraw)[jj * H + h])
-                             : __uint_as_float(sraw[jj * H + h]);
+      const float qsv = PRO ? qsc[PRO ? jj : 0][PRO ? h : 0]
+                            : SF16 ? f16_bits_to_f32(((const u16*)sraw)[jj * H + h])
+                                   : __uint_as_float(sraw[jj * H + h]);
       wqt[j][h] = f16_bits_to_f32(wv) * qsv;
     }
     idx_lds_barrier();
@@ -761,7 +992,18 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
     if (i + S::NB - 1 < nbw) issue_block(i + S::NB - 1);       // into the slot of block i - 1
     const int key0 = (blk0 + S::BSTR * i) * 32;                // span-relative first key
     if (span0 + key0 > maxp) break;                            // wave-uniform (never, by nbw)
-    const unsigned char* tile = ring + wave * S::NB * S::BB + (i % S::NB) * S::BB;
+    unsigned char* tile = ring + wave * S::NB * S::BB + (i % S::NB) * S::BB;
+    if constexpr (PRO) {
+      // a new key of the group in this block: its fresh codes replace the row the stream read
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        const int r = pg[jj] - span0 - key0;
+        if (jj < nq && r >= 0 && r < 32 && lane < D / 16)
+          *reinterpret_cast<uint4*>(tile + r * D + ((lane ^ (r & (S::CPR - 1))) << 4)) =
+              *reinterpret_cast<const uint4*>(&newk[jj][lane * 16]);
+      }
+      asm volatile("" ::: "memory");
+    }
     KFrag<FP8, D> kf;
     {
       v4i raw[S::CPR / 2];
@@ -838,10 +1080,41 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
       for (int i = 0; i < S::KPT; ++i) {
         const int e = tid + i * NT;
         if (e < n) {
-          const float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
+          float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
+          if constexpr (PRO) {
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj)
+              if (jj < nq && span0 + e == pg[jj]) ks = newks[jj];
+          }
           const float v = scl[j * SPAN + e] * ks;
           dst[e] = v;
           if (hj) atomicAdd(&hl[j * kHistBins + (order_key(v) >> 21)], 1u);
+        }
+      }
+    }
+    if constexpr (PRO) {
+      // the prolog's outputs: the group's query codes and scales (workgroup 0 of the sequence),
+      // the new key rows of this span
+      if (blockIdx.x == 0) {
+        const int qb = nq * H * D;                               // H == HT (compiled shapes)
+        for (int o = tid * 16; o < qb; o += NT * 16)
+          *reinterpret_cast<uint4*>(sa.pro.q_codes + (long)t0 * H * D + o) = *reinterpret_cast<const uint4*>(qsm + o);
+        for (int i = tid; i < nq * H; i += NT) {
+          const float v = qsc[i / H][i % H];
+          if (SF16) ((u16*)sa.pro.q_scale)[(long)t0 * H + i] = f32_to_f16_bits(v);
+          else ((float*)sa.pro.q_scale)[(long)t0 * H + i] = v;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        if (jj < nq && pg[jj] >= span0 && pg[jj] < span0 + nkeys) {
+          const long row = kv0 + pg[jj];
+          if (tid < D / 16)
+            *reinterpret_cast<uint4*>(sa.pro.k_cache + row * D + tid * 16) = *reinterpret_cast<const uint4*>(&newk[jj][tid * 16]);
+          if (tid == 0) {
+            if (SF16) ((u16*)sa.pro.k_scale)[row] = f32_to_f16_bits(newks[jj]);
+            else ((float*)sa.pro.k_scale)[row] = newks[jj];
+          }
         }
       }
     }
@@ -858,17 +1131,22 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
   }
 }
 
-template <int G, int D, bool FP8, bool DOTS>
+template <int G, int D, bool FP8, bool DOTS, bool PRO>
 static void launch_stream(const StreamArgs& sa, dim3 grid, hipStream_t st) {
-  if (sa.a.scale_f16) hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, true>), grid, dim3(kSNW * 64), 0, st, sa);
-  else hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, false>), grid, dim3(kSNW * 64), 0, st, sa);
+  if (sa.a.scale_f16) hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, true, PRO>), grid, dim3(kSNW * 64), 0, st, sa);
+  else hipLaunchKernelGGL((indexer_stream_kernel<G, D, FP8, DOTS, false, PRO>), grid, dim3(kSNW * 64), 0, st, sa);
 }
 
-template <int D, bool FP8, bool DOTS>
+template <int D, bool FP8, bool DOTS, bool PRO = false>
 static void launch_stream_g(int G, const StreamArgs& sa, dim3 grid, hipStream_t st) {
-  if (G == 1) launch_stream<1, D, FP8, DOTS>(sa, grid, st);
-  else if (G == 2) launch_stream<2, D, FP8, DOTS>(sa, grid, st);
-  else launch_stream<4, D, FP8, DOTS>(sa, grid, st);
+  if (G == 1) launch_stream<1, D, FP8, DOTS, PRO>(sa, grid, st);
+  else if (G == 2) launch_stream<2, D, FP8, DOTS, PRO>(sa, grid, st);
+  else launch_stream<4, D, FP8, DOTS, PRO>(sa, grid, st);
+}
+// raw query bytes the PRO kernel can stage for a group of G tokens
+static int pro_capacity(int G, int D) {
+  if (D == 128) return G == 1 ? ProStage<1, 128>::CAP : G == 2 ? ProStage<2, 128>::CAP : ProStage<4, 128>::CAP;
+  return G == 1 ? ProStage<1, 64>::CAP : G == 2 ? ProStage<2, 64>::CAP : ProStage<4, 64>::CAP;
 }
 
 }  // namespace dsa
@@ -920,7 +1198,8 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
                                  const void* q, const void* qs, const void* w, const void* k,
                                  const void* ks, float* scores, int32_t* dots, bool want_dots,
                                  long ld, uint32_t* hist, int hist_k, void* stream, const char* fn,
-                                 const dsa_paging* pg = nullptr) {
+                                 const dsa_paging* pg = nullptr, const dsa::ProArgs* pro = nullptr,
+                                 bool validate_only = false) {
   dsa_status st = check_batch(bt, fn, pg == nullptr);
   if (st != DSA_OK) return st;
   int bs_log2 = 0;
@@ -953,8 +1232,17 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
   const long gy = (long)bt->num_seqs * a.ngrp;
   if (gy > 65535L) return fail(DSA_ERR_INVALID_ARG, "%s: too many token groups", fn);
+  if (validate_only) return DSA_OK;
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = code == DSA_FP8_E4M3;
+  if (pro) {
+    if (a.ngrp != 1 || pg)
+      return fail(DSA_ERR_UNSUPPORTED, "%s: decode batches (at most 4 query tokens per sequence) on a flat cache only", fn);
+    const long rbytes = (long)G * H * D * (pro->in_bf16 ? 2 : 4);
+    if (rbytes > dsa::pro_capacity(G, D))
+      return fail(DSA_ERR_UNSUPPORTED, "%s: %d query tokens per sequence of %s rows exceed the in-kernel staging (%ld > %d bytes)",
+                  fn, bt->max_q_per_seq, pro->in_bf16 ? "bf16" : "fp32", rbytes, dsa::pro_capacity(G, D));
+  }
   if (a.ngrp == 1) {
     // decode: the streaming kernel, spans (multiples of 256 keys) sized for about one
     // workgroup per CU
@@ -964,9 +1252,17 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
     const long sg_max = dsa::stream_scl(G) / G / gk;
     if (sg < 1) sg = 1;
     if (sg > sg_max) sg = sg_max;
-    dsa::StreamArgs sa{a, (int)(sg * gk)};
+    dsa::StreamArgs sa{a, (int)(sg * gk), pro ? *pro : dsa::ProArgs{}};
     const dim3 grid((unsigned)((bt->max_kv_len + sa.span - 1) / sa.span), (unsigned)bt->num_seqs);
-    if (D == 128) {
+    if (pro) {
+      if (D == 128) {
+        if (fp8) dsa::launch_stream_g<128, true, false, true>(G, sa, grid, s);
+        else dsa::launch_stream_g<128, false, false, true>(G, sa, grid, s);
+      } else {
+        if (fp8) dsa::launch_stream_g<64, true, false, true>(G, sa, grid, s);
+        else dsa::launch_stream_g<64, false, false, true>(G, sa, grid, s);
+      }
+    } else if (D == 128) {
       if (want_dots) { if (fp8) return fail(DSA_ERR_UNSUPPORTED, "%s: int8 only", fn); dsa::launch_stream_g<128, false, true>(G, sa, grid, s); }
       else if (fp8) dsa::launch_stream_g<128, true, false>(G, sa, grid, s);
       else dsa::launch_stream_g<128, false, false>(G, sa, grid, s);
@@ -1019,6 +1315,68 @@ dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D,
                                    void* stream, const char* fn, const dsa_paging* paging) {
   return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
                         k_scale, scores, nullptr, false, ld, hist, k, stream, fn, paging);
+}
+
+dsa_status dsa_prolog_own_keys(const dsa_prolog_cfg* cfg, const dsa_batch* bt, const void* q_in,
+                               const float* q_cos, const float* q_sin, void* q_codes, void* q_scale,
+                               const void* k_in, void* k_cache, void* k_scale, void* stream);
+
+// Schedules of dsa_indexer_prolog_topk.  The in-kernel prolog repeats the group's query
+// quantization in every span workgroup of the sequence (measured on the part: about 3.4 us per
+// workgroup for 2 tokens x 64 heads of fp32 rows, against 2-5 us for a separate prolog launch),
+// so it is taken only where a sequence has few spans; the decision depends on the shapes alone.
+constexpr int kFusedMaxSpans = 16;
+
+// The indexer half of dsa_indexer_prolog_topk: the prolog (inside the streaming kernel, or as its
+// own launch), then the scores and the top-k's first radix pass.  cfg has been validated.
+dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_batch* batch,
+                                          const void* q_in, const float* q_cos, const float* q_sin,
+                                          const void* k_in, const void* w, void* q_codes, void* q_scale,
+                                          void* k_cache, void* k_scale, float* scores, int64_t ld,
+                                          uint32_t* hist, int32_t k, void* stream, const char* fn) {
+  dsa_status st = check_batch(batch, fn);
+  if (st != DSA_OK || batch->num_q == 0) return st;
+  if (!q_in || !k_in || !q_codes || !q_scale || !k_cache || !k_scale)
+    return fail(DSA_ERR_INVALID_ARG, "%s: a prolog pointer is NULL", fn);
+  if (cfg->rope_dim > 0 && (!q_cos || !q_sin)) return fail(DSA_ERR_INVALID_ARG, "%s: q_cos/q_sin is NULL", fn);
+  if (((uintptr_t)q_in | (uintptr_t)k_in) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q_in/k_in must be 16-byte aligned", fn);
+  if (((uintptr_t)q_cos | (uintptr_t)q_sin) & 3) return fail(DSA_ERR_INVALID_ARG, "%s: q_cos/q_sin must be 4-byte aligned", fn);
+  if (!((cfg->H == 64 && cfg->D == 128) || (cfg->H == 8 && cfg->D == 64)))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: (H, D) = (%d, %d) not compiled; supported (64,128), (8,64)", fn, cfg->H, cfg->D);
+  // the in-kernel form: decode groups whose raw query rows fit the staging, rope pairs inside a
+  // lane's 8 elements or 8-lane apart, and few spans per sequence
+  const int G = batch->max_q_per_seq >= 3 ? 4 : batch->max_q_per_seq;
+  const long rbytes = (long)G * cfg->H * cfg->D * (cfg->in_dtype == DSA_BF16 ? 2 : 4);
+  const int gk = 32 * dsa::kSNW;
+  long sg = ((long)(batch->max_kv_len + gk - 1) / gk * batch->num_seqs + 255) / 256;
+  sg = sg < 1 ? 1 : (sg > dsa::stream_scl(G) / G / gk ? dsa::stream_scl(G) / G / gk : sg);
+  const long spans = (batch->max_kv_len + sg * gk - 1) / (sg * gk);
+  bool in_kernel = batch->max_q_per_seq <= 4 && rbytes <= dsa::pro_capacity(G, cfg->D) &&
+                   (cfg->rope_dim == 0 || (cfg->rope_offset % 8 == 0 && cfg->rope_dim % 16 == 0)) &&
+                   spans <= kFusedMaxSpans;
+  if (const char* e = getenv("DSA_PROLOG_SCHEDULE")) {      // testing: force a schedule where legal
+    if (!strcmp(e, "separate")) in_kernel = false;
+    else if (!strcmp(e, "fused") && batch->max_q_per_seq <= 4 && rbytes <= dsa::pro_capacity(G, cfg->D) &&
+             (cfg->rope_dim == 0 || (cfg->rope_offset % 8 == 0 && cfg->rope_dim % 16 == 0)))
+      in_kernel = true;
+  }
+  if (!in_kernel) {
+    st = indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
+                        k_cache, k_scale, scores, nullptr, false, ld, hist, k, nullptr, fn, nullptr,
+                        nullptr, /*validate_only=*/true);
+    if (st != DSA_OK) return st;
+    st = dsa_prolog_own_keys(cfg, batch, q_in, q_cos, q_sin, q_codes, q_scale, k_in, k_cache, k_scale, stream);
+    if (st != DSA_OK) return st;
+    return indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
+                          k_cache, k_scale, scores, nullptr, false, ld, hist, k, stream, fn);
+  }
+  dsa::ProArgs p{};
+  p.q_in = q_in; p.k_in = k_in; p.cs = q_cos; p.sn = q_sin;
+  p.q_codes = (uint8_t*)q_codes; p.q_scale = q_scale; p.k_cache = (uint8_t*)k_cache; p.k_scale = k_scale;
+  p.in_bf16 = cfg->in_dtype == DSA_BF16; p.rope_dim = cfg->rope_dim; p.rope_offset = cfg->rope_offset;
+  p.rope_interleaved = cfg->rope_interleaved; p.hadamard = cfg->hadamard; p.round_scale = cfg->round_scale;
+  return indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
+                        k_cache, k_scale, scores, nullptr, false, ld, hist, k, stream, fn, nullptr, &p);
 }
 
 extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,

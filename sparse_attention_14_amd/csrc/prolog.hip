@@ -21,6 +21,8 @@ struct PrologArgs {
   const void* q_in; const float* q_cos; const float* q_sin; void* q_codes; void* q_scale;
   const void* k_in; const float* k_cos; const float* k_sin; const int64_t* k_slot;
   void* k_cache; void* k_scale;
+  // k_slot == NULL: key row r is token r's own key, at row kv_start[q_seq[r]] + q_pos[r]
+  const int32_t* q_seq; const int32_t* q_pos; const int64_t* kv_start;
 };
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
@@ -149,7 +151,10 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
   long drow;
   void* sdst;
   if (is_q) { dst = (uint8_t*)a.q_codes; drow = r_in; sdst = a.q_scale; }
-  else { drow = a.k_slot[r_in]; dst = (uint8_t*)a.k_cache; sdst = a.k_scale; }
+  else {
+    drow = a.k_slot ? a.k_slot[r_in] : a.kv_start[a.q_seq[r_in]] + a.q_pos[r_in];
+    dst = (uint8_t*)a.k_cache; sdst = a.k_scale;
+  }
   if (EPL == 2) {
     const uint16_t v = (uint16_t)code[0] | ((uint16_t)code[EPL - 1] << 8);
     ((uint16_t*)(dst + drow * D))[lane] = v;
@@ -164,6 +169,25 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
 
 }  // namespace dsa
 
+// Checks a prolog configuration (shared with dsa_indexer_prolog_topk).
+dsa_status dsa_check_prolog_cfg(const dsa_prolog_cfg* cfg, const char* fn) {
+  using dsa_host::fail;
+  if (!cfg) return fail(DSA_ERR_INVALID_ARG, "%s: cfg is NULL", fn);
+  const dsa_prolog_cfg c = *cfg;
+  if (c.D != 64 && c.D != 128) return fail(DSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, c.D);
+  if (c.H < 1 || c.H > 1024) return fail(DSA_ERR_INVALID_ARG, "%s: H out of range (got %d)", fn, c.H);
+  if (c.rope_dim < 0 || (c.rope_dim & 1) || c.rope_offset < 0 || c.rope_offset + c.rope_dim > c.D)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad rope_dim/rope_offset (%d, %d) for D=%d", fn,
+                c.rope_dim, c.rope_offset, c.D);
+  if (c.rope_interleaved != 0 && c.rope_interleaved != 1) return fail(DSA_ERR_INVALID_ARG, "%s: rope_interleaved must be 0/1", fn);
+  if (c.hadamard != 0 && c.hadamard != 1) return fail(DSA_ERR_INVALID_ARG, "%s: hadamard must be 0/1", fn);
+  if (c.round_scale != 0 && c.round_scale != 1) return fail(DSA_ERR_INVALID_ARG, "%s: round_scale must be 0/1", fn);
+  if (c.in_dtype != DSA_BF16 && c.in_dtype != DSA_F32) return fail(DSA_ERR_UNSUPPORTED, "%s: in_dtype must be BF16 or F32", fn);
+  if (c.code_dtype != DSA_I8 && c.code_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "%s: code_dtype must be I8 or FP8_E4M3", fn);
+  if (c.scale_dtype != DSA_F16 && c.scale_dtype != DSA_F32) return fail(DSA_ERR_UNSUPPORTED, "%s: scale_dtype must be F16 or F32", fn);
+  return DSA_OK;
+}
+
 extern "C" dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg, int32_t num_q,
                                          const void* q_in, const float* q_cos,
                                          const float* q_sin, void* q_codes, void* q_scale,
@@ -174,17 +198,8 @@ extern "C" dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg, int32_t num_
   if (!cfg) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: cfg is NULL");
   const dsa_prolog_cfg c = *cfg;
   if (num_q < 0 || num_k < 0) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: negative row count");
-  if (c.D != 64 && c.D != 128) return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_prolog: D must be 64 or 128 (got %d)", c.D);
-  if (c.H < 1 || c.H > 1024) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: H out of range (got %d)", c.H);
-  if (c.rope_dim < 0 || (c.rope_dim & 1) || c.rope_offset < 0 || c.rope_offset + c.rope_dim > c.D)
-    return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: bad rope_dim/rope_offset (%d, %d) for D=%d",
-                c.rope_dim, c.rope_offset, c.D);
-  if (c.rope_interleaved != 0 && c.rope_interleaved != 1) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: rope_interleaved must be 0/1");
-  if (c.hadamard != 0 && c.hadamard != 1) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: hadamard must be 0/1");
-  if (c.round_scale != 0 && c.round_scale != 1) return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: round_scale must be 0/1");
-  if (c.in_dtype != DSA_BF16 && c.in_dtype != DSA_F32) return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_prolog: in_dtype must be BF16 or F32");
-  if (c.code_dtype != DSA_I8 && c.code_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_prolog: code_dtype must be I8 or FP8_E4M3");
-  if (c.scale_dtype != DSA_F16 && c.scale_dtype != DSA_F32) return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_prolog: scale_dtype must be F16 or F32");
+  const dsa_status cst = dsa_check_prolog_cfg(cfg, "dsa_indexer_prolog");
+  if (cst != DSA_OK) return cst;
   if (num_q > 0 && (!q_in || !q_codes || !q_scale || (c.rope_dim && (!q_cos || !q_sin))))
     return fail(DSA_ERR_INVALID_ARG, "dsa_indexer_prolog: a query pointer is NULL");
   if (num_k > 0 && (!k_in || !k_slot || !k_cache || !k_scale || (c.rope_dim && (!k_cos || !k_sin))))
@@ -206,4 +221,28 @@ extern "C" dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg, int32_t num_
   if (c.D == 128) hipLaunchKernelGGL(dsa::prolog_kernel<2>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(dsa::prolog_kernel<1>, grid, dim3(256), 0, st, a);
   return dsa_host::check_launch("dsa_indexer_prolog");
+}
+
+// The prolog of a decode batch's query rows and of each token's own key row (cache row
+// kv_start[q_seq[t]] + q_pos[t], rotated with the token's table): the separate-launch schedule of
+// dsa_indexer_prolog_topk.  cfg and the pointers have been validated by the caller.
+dsa_status dsa_prolog_own_keys(const dsa_prolog_cfg* cfg, const dsa_batch* bt, const void* q_in,
+                               const float* q_cos, const float* q_sin, void* q_codes, void* q_scale,
+                               const void* k_in, void* k_cache, void* k_scale, void* stream) {
+  const dsa_prolog_cfg c = *cfg;
+  const long rows = (long)bt->num_q * (c.H + 1);
+  if (rows == 0) return DSA_OK;
+  dsa::PrologArgs a{};
+  a.H = c.H; a.D = c.D; a.rope_dim = c.rope_dim; a.rope_offset = c.rope_offset;
+  a.rope_interleaved = c.rope_interleaved; a.hadamard = c.hadamard; a.round_scale = c.round_scale;
+  a.in_bf16 = c.in_dtype == DSA_BF16; a.code_fp8 = c.code_dtype == DSA_FP8_E4M3;
+  a.scale_f16 = c.scale_dtype == DSA_F16; a.num_q = bt->num_q; a.num_k = bt->num_q;
+  a.q_in = q_in; a.q_cos = q_cos; a.q_sin = q_sin; a.q_codes = q_codes; a.q_scale = q_scale;
+  a.k_in = k_in; a.k_cos = q_cos; a.k_sin = q_sin; a.k_slot = nullptr; a.k_cache = k_cache;
+  a.k_scale = k_scale; a.q_seq = bt->q_seq; a.q_pos = bt->q_pos; a.kv_start = bt->kv_start;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipStream_t st = (hipStream_t)stream;
+  if (c.D == 128) hipLaunchKernelGGL(dsa::prolog_kernel<2>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(dsa::prolog_kernel<1>, grid, dim3(256), 0, st, a);
+  return DSA_OK;
 }

@@ -748,6 +748,40 @@ extern "C" dsa_status dsa_indexer_topk(const dsa_batch* bt, int32_t H, int32_t D
                       k_scale, scores, ld, k, idx, ws, ws_bytes, stream, "dsa_indexer_topk");
 }
 
+dsa_status dsa_check_prolog_cfg(const dsa_prolog_cfg* cfg, const char* fn);
+dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_batch* batch,
+                                          const void* q_in, const float* q_cos, const float* q_sin,
+                                          const void* k_in, const void* w, void* q_codes, void* q_scale,
+                                          void* k_cache, void* k_scale, float* scores, int64_t ld,
+                                          uint32_t* hist, int32_t k, void* stream, const char* fn);
+
+// dsa_indexer_prolog followed by dsa_indexer_topk; where the shapes suit it the prolog runs inside
+// the indexer kernel (each indexer workgroup quantizes its sequence's query rows itself and the
+// workgroup whose key span holds a token's own position quantizes that token's new key row).
+extern "C" dsa_status dsa_indexer_prolog_topk(const dsa_prolog_cfg* cfg, const dsa_batch* bt,
+                                              const void* q_in, const float* q_cos,
+                                              const float* q_sin, const void* k_in, const void* w,
+                                              void* q_codes, void* q_scale, void* k_cache,
+                                              void* k_scale, int32_t k, float* scores, int64_t ld,
+                                              int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_indexer_prolog_topk";
+  dsa_status st = dsa_check_prolog_cfg(cfg, fn);
+  if (st != DSA_OK) return st;
+  dsa::TkArgs a{};
+  st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a);
+  if (st != DSA_OK) return st;
+  st = dsa_indexer_prolog_scores_hist(cfg, bt, q_in, q_cos, q_sin, k_in, w, q_codes, q_scale, k_cache,
+                                      k_scale, scores, ld, bt->num_q ? a.hist : nullptr, k, stream, fn);
+  if (st != DSA_OK || bt->num_q == 0) return st;
+  if (a.T >= dsa::kRowMinT) {
+    a.row_hist = 1;
+    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, (hipStream_t)stream, a);
+  } else {
+    topk_tail(a, (hipStream_t)stream);
+  }
+  return dsa_host::check_launch(fn);
+}
+
 extern "C" dsa_status dsa_indexer_topk_paged(const dsa_batch* bt, const dsa_paging* paging,
                                              int32_t H, int32_t D, dsa_dtype code_dtype,
                                              dsa_dtype scale_dtype, const void* q_codes,

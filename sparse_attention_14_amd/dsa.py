@@ -260,6 +260,52 @@ def dsa_indexer_topk(batch: Batch, H: int, D: int, code: str, scale_dt: str, q_c
     return idx
 
 
+def dsa_indexer_prolog_topk(batch: Batch, H: int, D: int, code: str, scale_dt: str, *, q_in, k_in,
+                            w, q_codes, q_scale, k_cache, k_scale, k: int, q_cos=None, q_sin=None,
+                            rope_dim=0, rope_offset=0, rope_interleaved=False, hadamard=False,
+                            round_scale=False, scores: Optional[torch.Tensor] = None,
+                            idx: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prolog of the batch's query rows and of each token's own key row (written at cache row
+    kv_start[q_seq[t]] + q_pos[t]), indexer scores and top-k in one call -> idx int32 [T, k].
+    q_codes/q_scale receive the quantized query; `scores` is written as by dsa_indexer_scores."""
+    if code not in _CODE or scale_dt not in _SCALE:
+        raise ValueError("code must be 'i8'|'e4m3', scale_dt 'f16'|'f32'")
+    T = batch.num_q
+    ct, st = _CODE_TORCH[code], _SCALE_TORCH[scale_dt]
+    in_dt = q_in.dtype
+    if in_dt not in (torch.bfloat16, torch.float32):
+        raise ValueError("inputs must be bf16 or fp32")
+    _need(q_in, "q_in", in_dt, (T, H, D))
+    _need(k_in, "k_in", in_dt, (T, D))
+    _need(w, "w", torch.float16, (T, H))
+    _need(q_codes, "q_codes", ct, (T, H, D))
+    _need(q_scale, "q_scale", st, (T, H))
+    _need(k_cache, "k_cache", ct)
+    _need(k_scale, "k_scale", st)
+    if rope_dim:
+        _need(q_cos, "q_cos", torch.float32, (T, rope_dim // 2))
+        _need(q_sin, "q_sin", torch.float32, (T, rope_dim // 2))
+    if scores is None:
+        scores = torch.empty((T, _scores_ld(batch.max_kv_len)), dtype=torch.float32, device=q_in.device)
+    _need(scores, "scores", torch.float32)
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_in.device)
+    _need(idx, "idx", torch.int32, (T, k))
+    if ws is None:
+        ws = _workspace(dsa_topk_workspace_size(T, batch.max_kv_len, k), q_in.device)
+    _need(ws, "ws", torch.uint8)
+    cfg = DsaPrologCfg(H, D, rope_dim, rope_offset, int(rope_interleaved), int(hadamard),
+                       int(round_scale), DSA_BF16 if in_dt == torch.bfloat16 else DSA_F32,
+                       _CODE[code], _SCALE[scale_dt])
+    b = batch.c()
+    check("dsa_indexer_prolog_topk", lib.dsa_indexer_prolog_topk(
+        ctypes.byref(cfg), ctypes.byref(b), _ptr(q_in), _ptr(q_cos), _ptr(q_sin), _ptr(k_in), _ptr(w),
+        _ptr(q_codes), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), k, _ptr(scores),
+        scores.shape[1] if scores.dim() == 2 else 0, _ptr(idx), _ptr(ws), ws.numel(), _stream()))
+    return idx
+
+
 def dsa_sparse_attn_decode(batch: Batch, q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
                            sink: Optional[torch.Tensor], scale: float,
                            out: Optional[torch.Tensor] = None,

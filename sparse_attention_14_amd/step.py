@@ -1,4 +1,5 @@
-"""One DSA decode step through the C ABI: prolog -> indexer scores + top-k -> sparse attention.
+"""One DSA decode step through the C ABI: prolog -> indexer scores + top-k -> sparse attention
+(the prolog inside the indexer kernel where the library supports that form).
 
 [DIA] "Deepseek Indexer Attention" (jsqmd.com/news/787325): the decode layer runs the indexer
 prolog, the Lightning Indexer with its TopK and Sparse Flash Attention in that order (the MLA
@@ -12,8 +13,9 @@ from typing import Optional
 
 import torch
 
-from .dsa import (Batch, _scores_ld, dsa_indexer_prolog, dsa_indexer_topk,
-                  dsa_sparse_attn_decode, dsa_sparse_attn_workspace_size,
+from ._lib import DSA_ERR_UNSUPPORTED, DsaError
+from .dsa import (Batch, _scores_ld, dsa_indexer_prolog, dsa_indexer_prolog_topk,
+                  dsa_indexer_topk, dsa_sparse_attn_decode, dsa_sparse_attn_workspace_size,
                   dsa_topk_workspace_size)
 
 
@@ -59,20 +61,37 @@ class StepBuffers:
 
 def decode_step(batch: Batch, cfg: IndexerCfg, *, q_in, k_in, new_slots, w, k_cache, k_scale,
                 q_attn, kv, sink, scale: float, buf: StepBuffers, q_cos=None, q_sin=None,
-                k_cos=None, k_sin=None) -> torch.Tensor:
+                k_cos=None, k_sin=None, fused: bool = True) -> torch.Tensor:
     """Run the four stages for the batch's query tokens.
 
     q_in [T, H, D] / k_in [T, D]: raw indexer query / key activations of the new tokens
-    (bf16 or fp32); new_slots [T] int64: cache rows of the new tokens' keys; k_cache/k_scale:
-    the quantized indexer key cache; q_attn [T, Hq, 576] bf16, kv [N, 576] bf16, sink [Hq].
-    Returns buf.out [T, Hq, 512] bf16.
+    (bf16 or fp32); new_slots [T] int64: cache rows of the new tokens' keys (row
+    kv_start[q_seq[t]] + q_pos[t] of the batch layout); k_cache/k_scale: the quantized indexer
+    key cache; q_attn [T, Hq, 576] bf16, kv [N, 576] bf16, sink [Hq].
+    With `fused` the prolog runs inside the indexer kernel (dsa_indexer_prolog_topk; the keys'
+    rotary tables are the tokens' own, q_cos/q_sin) wherever the library supports that form, and
+    as its own launch otherwise.  Returns buf.out [T, Hq, 512] bf16.
     """
-    dsa_indexer_prolog(cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, q_cos=q_cos,
-                       q_sin=q_sin, q_codes=buf.q_codes, q_scale=buf.q_scale, k_in=k_in,
-                       k_cos=k_cos, k_sin=k_sin, k_slot=new_slots, k_cache=k_cache,
-                       k_scale=k_scale, rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
-                       rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard)
-    dsa_indexer_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
-                     k_cache, k_scale, cfg.k, scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
+    done = False
+    if fused:
+        try:
+            dsa_indexer_prolog_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, k_in=k_in,
+                                    w=w, q_codes=buf.q_codes, q_scale=buf.q_scale, k_cache=k_cache,
+                                    k_scale=k_scale, k=cfg.k, q_cos=q_cos, q_sin=q_sin,
+                                    rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
+                                    rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard,
+                                    scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
+            done = True
+        except DsaError as e:
+            if e.status != DSA_ERR_UNSUPPORTED:
+                raise
+    if not done:
+        dsa_indexer_prolog(cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, q_cos=q_cos,
+                           q_sin=q_sin, q_codes=buf.q_codes, q_scale=buf.q_scale, k_in=k_in,
+                           k_cos=k_cos, k_sin=k_sin, k_slot=new_slots, k_cache=k_cache,
+                           k_scale=k_scale, rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
+                           rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard)
+        dsa_indexer_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
+                         k_cache, k_scale, cfg.k, scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
     return dsa_sparse_attn_decode(batch, q_attn, kv, buf.idx, sink, scale, out=buf.out,
                                   ws=buf.ws_sfa)

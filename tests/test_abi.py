@@ -94,6 +94,17 @@ def test_validation_errors_before_any_device_call():
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, P, P, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
     cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 8, P, None, None, P, P, 0, None, None, None, None, None, None, None) == L.DSA_ERR_INVALID_ARG
+    # fused prolog + indexer + top-k: cfg checks first, then the fused form's own limits, then top-k
+    assert lib.dsa_indexer_prolog_topk(None, ctypes.byref(b), P, P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
+    cfg = L.DsaPrologCfg(32, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(cfg), ctypes.byref(b), P, P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
+    assert b"not compiled" in lib.dsa_last_error()
+    cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, 99, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(cfg), ctypes.byref(b), P, P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED
+    cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(cfg), ctypes.byref(b), P, P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 16, None) == L.DSA_ERR_WORKSPACE
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(cfg), ctypes.byref(b), None, P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(cfg), ctypes.byref(b), ctypes.c_void_p(0x1008), P, P, P, P, P, P, P, P, 2048, P, 65536, P, P, 1 << 30, None) == L.DSA_ERR_INVALID_ARG
     # fp8 contraction hook: unknown path, ragged sizes, bad depth, misaligned operand; empty is a no-op
     assert lib.dsa_e4m3_dots(P, 32, P, 32, 128, 3, P, None) == L.DSA_ERR_INVALID_ARG
     assert lib.dsa_e4m3_dots(P, 33, P, 32, 128, 0, P, None) == L.DSA_ERR_INVALID_ARG
@@ -109,6 +120,8 @@ def test_empty_batches_are_noops_without_device():
     assert lib.dsa_indexer_scores(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_topk(ctypes.byref(b), None, 0, 2048, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_indexer_topk(ctypes.byref(b), 64, 128, L.DSA_I8, L.DSA_F16, None, None, None, None, None, None, 0, 2048, None, None, 0, None) == L.DSA_OK
+    pcfg = L.DsaPrologCfg(64, 128, 0, 0, 0, 0, 0, L.DSA_F32, L.DSA_I8, L.DSA_F16)
+    assert lib.dsa_indexer_prolog_topk(ctypes.byref(pcfg), ctypes.byref(b), None, None, None, None, None, None, None, None, None, 2048, None, 0, None, None, 0, None) == L.DSA_OK
     assert lib.dsa_sparse_attn_decode(ctypes.byref(b), 128, None, None, 576, None, 2048, None, ctypes.c_float(0.04), None, None, 0, None) == L.DSA_OK
     cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_FP8_E4M3, L.DSA_F16)
     assert lib.dsa_indexer_prolog(ctypes.byref(cfg), 0, None, None, None, None, None, 0, None, None, None, None, None, None, None) == L.DSA_OK
