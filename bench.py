@@ -353,7 +353,9 @@ def main():
     # flops), where the keys and gathered rows come from the caches
     prefill = wl.max_q_per_seq > 4
     idx_peak = INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS
-    single = {"indexer": ("dsa::indexer_kernel", b_indexer, idx_ops, idx_peak),
+    # decode batches (at most 4 query tokens per sequence) take the streaming indexer kernel
+    idx_kernel = "dsa::indexer_stream_kernel" if wl.max_q_per_seq <= 4 else "dsa::indexer_kernel"
+    single = {"indexer": (idx_kernel, b_indexer, idx_ops, idx_peak),
               "sfa_split": ("dsa::sfa_kernel", n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4,
                             sfa_flops, BF16_PEAK_TFLOPS)}
     dominant = max(single, key=lambda n: stage_us[n])
