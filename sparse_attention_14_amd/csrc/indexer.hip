@@ -505,6 +505,133 @@ static void launch_g(int G, const IdxArgs& a, dim3 grid, hipStream_t st) {
 }
 
 
+// Sum of lane l and lane l ^ 32 (the two 16-head halves of an MFMA column), in every lane.
+__device__ __forceinline__ float add_half_swap(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Prefill kernel: many query tokens per sequence, int8 codes, 64 heads x 128 dims (flat or paged).
+// [LI] "Lightning Indexer" (jsqmd.com/news/787325): at prefill the indexer is a dense int8 GEMM
+// per head over the chunk's tokens and the cached keys, then ReLU and the head-weighted sum.
+//
+// Workgroup = (sequence, tile of kPT query tokens).  The tile's query codes and w * q_scale stay
+// in LDS; its eight waves split the keys the tile sees into kPG-key groups (wave w takes groups
+// w, w + 8, ...).  A wave holds one group's key codes in registers, loaded straight from memory
+// with the next group's loads in flight, and runs every token of the tile against them:
+// 16 v_mfma_i32_32x32x32_i8 per token (2 head blocks x 2 key blocks x 4 depth steps, query
+// fragments from LDS), then the ReLU-weighted head sum (3 VALU ops per (token, head, key) --
+// the kernel's bound) and the key scale.  Each key group is read once per kPT tokens (the
+// decode-shaped tile kernel reads it once per 4).  Causality: a token skips the groups past its
+// position (wave-uniform) and masks the keys past it inside the last one.
+constexpr int kPT = 16;                        // query tokens per prefill workgroup
+constexpr int kPG = 64;                        // keys per wave group
+constexpr int kPW = 12;                        // waves per prefill workgroup (3 per SIMD)
+
+__global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
+  constexpr int H = 64, D = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kPT * H * D];       // 128 KiB
+  __shared__ __attribute__((aligned(16))) float wq[kPT][H];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hv = lane >> 5, col = lane & 31;
+  const int b = blockIdx.y;
+  const int q0 = a.q_start[b];
+  const int nseq = a.q_start[b + 1] - q0;
+  if ((int)blockIdx.x * kPT >= nseq) return;                 // whole workgroup, before any barrier
+  const int t0 = q0 + blockIdx.x * kPT;
+  const int nt = min(kPT, nseq - (int)blockIdx.x * kPT);
+  // the tile's positions as a lane vector (token j in lane j), its largest position
+  const int pl = lane < nt ? a.q_pos[t0 + lane] : -1;
+  int maxp = pl;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) maxp = max(maxp, __shfl_xor(maxp, m, kWave));
+  const long kv0 = a.bt ? 0 : a.kv_start[b];               // paged: rows through the block table
+  // stage the tile's query codes (row r's 16-byte chunk c at chunk c ^ (r % 8): the 32 rows one
+  // fragment read touches then spread over all banks) and head weights
+  for (int o = tid * 16; o < nt * H * D; o += kPW * 64 * 16) {
+    const int r = o >> 7, c = (o >> 4) & 7;
+    *reinterpret_cast<uint4*>(qs + r * D + ((c ^ (r & 7)) << 4)) =
+        *reinterpret_cast<const uint4*>(a.q_codes + (long)t0 * H * D + o);
+  }
+  for (int i = tid; i < nt * H; i += kPW * 64) {
+    const long ti = (long)t0 * H + i;
+    const float qsv = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.q_scale)[ti]) : ((const float*)a.q_scale)[ti];
+    wq[i / H][i % H] = f16_bits_to_f32(a.w[ti]) * qsv;
+  }
+  __syncthreads();
+
+  const int ngroups = (maxp + 1 + kPG - 1) / kPG;
+  auto load_group = [&](int g, v4i (&kf)[2][4], float (&ks)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int pos = min(g * kPG + 32 * kb + col, maxp);     // positions past maxp: masked below
+      const long row = a.bt ? ((long)a.bt[(long)b * a.bps + (pos >> a.bs_log2)] << a.bs_log2) +
+                                  (pos & ((1 << a.bs_log2) - 1))
+                            : kv0 + pos;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        kf[kb][q] = *reinterpret_cast<const v4i*>(a.k_cache + row * D + 32 * q + 16 * hv);
+      ks[kb] = a.scale_f16 ? f16_bits_to_f32(((const u16*)a.k_scale)[row]) : ((const float*)a.k_scale)[row];
+    }
+  };
+  auto load_q = [&](int j, v4i (&qf)[2][4]) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        qf[mb][q] = *reinterpret_cast<const v4i*>(qs + (j * H + 32 * mb + col) * D +
+                                                  (((2 * q + hv) ^ (col & 7)) << 4));
+  };
+  v4i kf[2][4], kn[2][4];
+  float ks[2], ksn[2];
+  if (wave < ngroups) load_group(wave, kn, ksn);
+  for (int g = wave; g < ngroups; g += kPW) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      ks[kb] = ksn[kb];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kf[kb][q] = kn[kb][q];
+    }
+    if (g + kPW < ngroups) load_group(g + kPW, kn, ksn);     // in flight under this group's tokens
+    const int key0 = g * kPG;
+    for (int j = 0; j < nt; ++j) {
+      const int p = __builtin_amdgcn_readlane(pl, j);
+      if (key0 > p) continue;
+      v4i qa[2][4];
+      load_q(j, qa);
+      float sum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        v16i acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[mb][q], kf[0][q], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[mb][q], kf[1][q], acc1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 w4 = *reinterpret_cast<const float4*>(&wq[j][32 * mb + 8 * i + 4 * hv]);
+          const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sum[0][r] = fmaf(wv[r], (float)max(acc0[4 * i + r], 0), sum[0][r]);
+            sum[1][r] = fmaf(wv[r], (float)max(acc1[4 * i + r], 0), sum[1][r]);
+          }
+        }
+      }
+      const float s0v = add_half_swap((sum[0][0] + sum[0][1]) + (sum[0][2] + sum[0][3]));
+      const float s1v = add_half_swap((sum[1][0] + sum[1][1]) + (sum[1][2] + sum[1][3]));
+      if (hv == 0) {
+        float* dst = a.scores + (long)(t0 + j) * a.ld;
+        const int k0 = key0 + col, k1 = key0 + 32 + col;
+        if (k0 <= p) dst[k0] = s0v * ks[0];
+        if (k1 <= p) dst[k1] = s1v * ks[1];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Prolog inside the streaming kernel (dsa_indexer_prolog_topk).  [PRO] "Indexer Prolog"
 // (jsqmd.com/news/787325): the query and the new cache key are quantized per token-head after
@@ -683,11 +810,6 @@ __device__ __forceinline__ void wait_blocks_after(int n) {
 // 4 bytes at base + off (base wave-uniform in SGPRs) into LDS at lds_addr + 4 * lane
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, unsigned lds_addr) {
   asm volatile("global_load_lds_dword %0, %1" :: "v"(off), "s"(base), "{m0}"(lds_addr));
-}
-// Sum of lane l and lane l ^ 32 (the two 16-head halves of an MFMA column), in every lane.
-__device__ __forceinline__ float add_half_swap(float v) {
-  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(x[0]) + __uint_as_float(x[1]);
 }
 
 struct StreamArgs {
@@ -1271,6 +1393,13 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
       else if (fp8) dsa::launch_stream_g<64, true, false>(G, sa, grid, s);
       else dsa::launch_stream_g<64, false, false>(G, sa, grid, s);
     }
+    return dsa_host::check_launch(fn);
+  }
+  if (!want_dots && !fp8 && !hist && H == 64 && D == 128) {
+    // many tokens per sequence, no fused histogram (the top-k's row workgroups build their own):
+    // the prefill kernel, one workgroup per (sequence, tile of kPT tokens)
+    const dim3 pgrid((unsigned)((bt->max_q_per_seq + dsa::kPT - 1) / dsa::kPT), (unsigned)bt->num_seqs);
+    hipLaunchKernelGGL(dsa::indexer_prefill_kernel, pgrid, dim3(dsa::kPW * 64), 0, s, a);
     return dsa_host::check_launch(fn);
   }
   const dim3 grid((unsigned)((bt->max_kv_len + dsa::kCK - 1) / dsa::kCK), (unsigned)gy);

@@ -694,6 +694,19 @@ static void topk_tail(const dsa::TkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(dsa::topk_finalize, grid, dim3(dsa::kNT), 0, s, a);
 }
 
+// The top-k after the scores: one workgroup per row for many-row batches (it builds its own
+// histogram), else (histogram pass unless the indexer accumulated it) select + finalize.
+static void topk_after_scores(dsa::TkArgs& a, bool rows, bool hist_done, hipStream_t s) {
+  if (rows) {
+    a.row_hist = 0;
+    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, s, a);
+    return;
+  }
+  if (!hist_done)
+    hipLaunchKernelGGL(dsa::topk_hist, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
+  topk_tail(a, s);
+}
+
 extern "C" dsa_status dsa_topk(const dsa_batch* bt, const float* scores, int64_t ld, int32_t k,
                                int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "dsa_topk";
@@ -729,17 +742,15 @@ static dsa_status indexer_topk(const dsa_batch* bt, const dsa_paging* pg, int32_
   // many rows take one workgroup per row, which builds its row's histogram itself: there the
   // indexer's many small workgroups would each flush thousands of bins with global atomics
   // (measured on the prefill chunk: ~0.7 ms of atomics against ~0.1 ms for the row workgroups).
+  // Only the streaming (decode) indexer accumulates the histogram; batches with more than 4
+  // tokens per sequence get it from their own pass.
   const bool rows = bt->num_q >= dsa::kRowMinT;
+  const bool fused_hist = !rows && bt->max_q_per_seq <= 4;
   st = dsa_indexer_scores_hist(bt, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
-                               k_scale, scores, ld, bt->num_q && !rows ? a.hist : nullptr, k, stream,
-                               fn, pg);
+                               k_scale, scores, ld, bt->num_q && fused_hist ? a.hist : nullptr, k,
+                               stream, fn, pg);
   if (st != DSA_OK || bt->num_q == 0) return st;
-  if (rows) {
-    a.row_hist = 0;
-    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, (hipStream_t)stream, a);
-  } else {
-    topk_tail(a, (hipStream_t)stream);
-  }
+  topk_after_scores(a, rows, fused_hist, (hipStream_t)stream);
   return dsa_host::check_launch(fn);
 }
 
@@ -776,16 +787,12 @@ extern "C" dsa_status dsa_indexer_prolog_topk(const dsa_prolog_cfg* cfg, const d
   st = topk_prepare(bt, scores, ld, k, idx, ws, ws_bytes, fn, &a);
   if (st != DSA_OK) return st;
   const bool rows = bt->num_q >= dsa::kRowMinT;     // one workgroup per row: own histogram
+  const bool fused_hist = !rows && bt->max_q_per_seq <= 4;
   st = dsa_indexer_prolog_scores_hist(cfg, bt, q_in, q_cos, q_sin, k_in, w, q_codes, q_scale, k_cache,
-                                      k_scale, scores, ld, bt->num_q && !rows ? a.hist : nullptr, k,
-                                      stream, fn);
+                                      k_scale, scores, ld, bt->num_q && fused_hist ? a.hist : nullptr,
+                                      k, stream, fn);
   if (st != DSA_OK || bt->num_q == 0) return st;
-  if (rows) {
-    a.row_hist = 0;
-    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, (hipStream_t)stream, a);
-  } else {
-    topk_tail(a, (hipStream_t)stream);
-  }
+  topk_after_scores(a, rows, fused_hist, (hipStream_t)stream);
   return dsa_host::check_launch(fn);
 }
 
