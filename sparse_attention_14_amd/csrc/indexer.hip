@@ -445,46 +445,20 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   }
   if constexpr (!DOTS) {
     __syncthreads();
-    // With the top-k's first radix pass fused (a.hist): a histogram of the top 11 key bits of
-    // this chunk's scores per token, in LDS (reusing the key buffer, free after the barrier
-    // above), taken from the values as they are stored; its non-zero bins are then added to
-    // one of the token's histogram shards.  Rows with at most hist_k valid keys get none.
-    uint32_t* hl = reinterpret_cast<uint32_t*>(kl);
-    static_assert(G * kHistBins * 4 <= KB, "histogram does not fit the key buffer");
-    if (a.hist) {
-      for (int i = threadIdx.x * 4; i < G * kHistBins; i += NT * 4)
-        *reinterpret_cast<uint4*>(hl + i) = uint4{0u, 0u, 0u, 0u};
-      __syncthreads();
-    }
     // coalesced score stores, times the key scales: token j of the group, keys chunk0 ..
     // min(chunk0 + kCK, p_j + 1)
     for (int j = 0; j < G; ++j) {
       const int tj = q_lo + j;
       if (tj >= q_hi) break;
       const int n = min(kCK, pg[j] + 1 - chunk0);
-      const bool hj = a.hist && pg[j] + 1 > a.hist_k;
       float* dst = a.scores + (long)tj * a.ld + chunk0;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int e = (int)threadIdx.x + i * NT;
         if (e < n) {
           const float ks = SF16 ? f16_bits_to_f32((u16)ksraw[i]) : __uint_as_float(ksraw[i]);
-          const float v = scl[j][e] * ks;
-          dst[e] = v;
-          if (hj) atomicAdd(&hl[j * kHistBins + (order_key(v) >> 21)], 1u);
+          dst[e] = scl[j][e] * ks;
         }
-      }
-    }
-    if (a.hist) {
-      __syncthreads();
-      // consecutive bins in consecutive lanes, so that a wave's atomics fall in few lines; only
-      // non-zero bins reach global memory
-      uint32_t* gh = a.hist + (long)blockIdx.x % kHistShards * kHistBins;
-      for (int i = threadIdx.x; i < G * kHistBins; i += NT) {
-        const int j = i / kHistBins;
-        const uint32_t c = hl[i];
-        if (c && q_lo + j < q_hi)
-          atomicAdd(gh + (long)(q_lo + j) * kHistShards * kHistBins + (i % kHistBins), c);
       }
     }
   }
@@ -1357,6 +1331,8 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   if (validate_only) return DSA_OK;
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = code == DSA_FP8_E4M3;
+  // only the streaming kernel accumulates the top-k's histogram (decode groups)
+  if (hist && a.ngrp != 1) return fail(DSA_ERR_UNSUPPORTED, "%s: fused histogram needs at most 4 tokens per sequence", fn);
   if (pro) {
     if (a.ngrp != 1 || pg)
       return fail(DSA_ERR_UNSUPPORTED, "%s: decode batches (at most 4 query tokens per sequence) on a flat cache only", fn);

@@ -6,7 +6,7 @@
 // workgroups, so a decode batch of 8 rows still occupies the whole chip:
 //
 //   hist    : the top 11 bits of every key, per row, in a 2048-bin histogram (its own pass,
-//             or fused into the indexer workgroups by dsa_indexer_topk)
+//             or, for decode batches, fused into the streaming indexer by dsa_indexer_topk)
 //   select  : one workgroup per 4096-score chunk derives the digit b1 that holds the k-th
 //             largest key; positions above b1 go into the chunk's position bitmap, positions
 //             with digit b1 (candidates, 1-3 % of a Gaussian-like row) into the chunk's
@@ -55,7 +55,6 @@ constexpr int kRowMinT = 256;        // batches of at least this many rows take 
 struct TkArgs {
   const int32_t* q_pos; const float* scores; long ld; int k; int T; int nch;
   int32_t* idx; uint32_t* hist; uint32_t* bg; uint32_t* cnt; uint32_t* bits; uint64_t* slots;
-  int row_hist;                      // topk_row: hist holds the indexer's row histograms
 };
 
 // Keeps the loads issued above it in place: the compiler would otherwise sink loads that only
@@ -374,8 +373,9 @@ __device__ __forceinline__ float f4get(const float4& v, int r) {
 __device__ __forceinline__ void issue_fence_row() { asm volatile("" ::: "memory"); }
 
 // Many-row batches (a prefill chunk: thousands of rows): one workgroup per row finishes the
-// selection on its own, with no second launch.  One memory round trip brings the row histogram
-// and the row's first 65536 scores (registers); every key with digit >= b1 is compacted into
+// selection on its own, with no second launch.  One memory round trip brings the row's first
+// 65536 scores (registers), from which the workgroup builds the row's first-digit histogram in
+// LDS (later segments are streamed again); every key with digit >= b1 is compacted into
 // LDS in position order (an ordered prefix over (float4 slot, thread)); two more digits over the
 // candidates give K*; the selection is one ordered pass over the compacted list.  Rows with more
 // entries than LDS holds re-read the row for each pass.  On a decode batch of a few rows this
@@ -390,20 +390,8 @@ __global__ void __launch_bounds__(kRNT) topk_row(TkArgs a) {
   const int t = blockIdx.x, tid = threadIdx.x;
   const int k = a.k;
   const float* row = a.scores + (long)t * a.ld;
-  // ---- one round trip: q_pos, the row histogram and the first segment
+  // ---- one round trip: q_pos and the first segment
   const int p = a.q_pos[t];
-  uint32_t hv[2] = {0u, 0u};
-  uint32_t hv2[2] = {0u, 0u};
-  {
-    // loaded unconditionally (the workspace rows are zero when the indexer did not fill them), so
-    // that every load of the round trip is issued before the first wait
-    const uint32_t* gh = a.hist + (long)t * kShards * kBins;
-#pragma unroll
-    for (int sd = 0; sd < kShards; ++sd) {
-      hv[0] += gh[sd * kBins + tid]; hv[1] += gh[sd * kBins + kRNT + tid];
-      hv2[0] += gh[sd * kBins + 2 * kRNT + tid]; hv2[1] += gh[sd * kBins + 3 * kRNT + tid];
-    }
-  }
   float4 v[kRJ];
   load_seg(v, row, a.ld, 0);
   issue_fence_row();
@@ -414,15 +402,8 @@ __global__ void __launch_bounds__(kRNT) topk_row(TkArgs a) {
   }
   const int L = p + 1;
   const int nseg = (L + kSeg - 1) / kSeg;
-  // ---- the first digit: the indexer's histogram (cleared for the next call), or built here
-  if (a.row_hist) {
-    h[tid] = hv[0]; h[kRNT + tid] = hv[1]; h[2 * kRNT + tid] = hv2[0]; h[3 * kRNT + tid] = hv2[1];
-    uint32_t* gh = a.hist + (long)t * kShards * kBins;
-#pragma unroll
-    for (int sd = 0; sd < kShards; ++sd)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) gh[sd * kBins + q * kRNT + tid] = 0u;
-  } else {
+  // ---- the first digit's histogram over the row
+  {
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q * kRNT + tid] = 0u;
     __syncthreads();
@@ -698,7 +679,6 @@ static void topk_tail(const dsa::TkArgs& a, hipStream_t s) {
 // histogram), else (histogram pass unless the indexer accumulated it) select + finalize.
 static void topk_after_scores(dsa::TkArgs& a, bool rows, bool hist_done, hipStream_t s) {
   if (rows) {
-    a.row_hist = 0;
     hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, s, a);
     return;
   }
@@ -715,7 +695,6 @@ extern "C" dsa_status dsa_topk(const dsa_batch* bt, const float* scores, int64_t
   if (st != DSA_OK || bt->num_q == 0) return st;
   hipStream_t s = (hipStream_t)stream;
   if (a.T >= dsa::kRowMinT) {                            // the row workgroups build their histograms
-    a.row_hist = 0;
     hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, s, a);
     return dsa_host::check_launch(fn);
   }
