@@ -33,6 +33,13 @@
  *  - A call with zero query tokens (or zero rows) is a successful no-op.
  *  - Calls on the same stream are ordered; calls that share a workspace buffer must not run
  *    concurrently on different streams.
+ *  - Debug mode for read-before-write races: with the environment variable DSA_DEBUG_POISON=1
+ *    (read at each call) the indexer, top-k and attention kernels fill their LDS with all-one
+ *    bytes (NaN as a float, -1 as an integer) before use, and the calls fill the workspace
+ *    regions their kernels write before reading (top-k candidate slots, attention split
+ *    partials) the same way with an extra fill kernel on `stream`.  Results must not change;
+ *    a read of data that was never written shows up as NaN, -1 or a wrong selection.  Slower;
+ *    never for production.  The projection kernels (dynamic LDS) are not covered.
  */
 #ifndef DSA_H
 #define DSA_H

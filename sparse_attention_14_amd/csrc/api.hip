@@ -1,6 +1,7 @@
 // Host-side plumbing shared by the C ABI entry points: thread-local error text, launch checks.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "common.h"
 
@@ -24,6 +25,26 @@ dsa_status check_launch(const char* what) {
   return DSA_OK;
 }
 
+bool debug_poison() {
+  const char* e = getenv("DSA_DEBUG_POISON");
+  return e && e[0] == '1';
+}
+
+}  // namespace dsa_host
+
+namespace dsa {
+__global__ void __launch_bounds__(256) fill_ones(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0xFFFFFFFFu;
+}
+}  // namespace dsa
+
+namespace dsa_host {
+void poison_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (!p || n == 0) return;
+  const unsigned blocks = (unsigned)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+  hipLaunchKernelGGL(dsa::fill_ones, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, n);
+}
 }  // namespace dsa_host
 
 extern "C" const char* dsa_last_error(void) { return g_err; }

@@ -121,6 +121,14 @@ __device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* s
   __syncthreads();
 }
 
+// Debug poisoning (DSA_DEBUG_POISON=1, race detection): fill an LDS object with all-one bytes --
+// NaN as fp32/bf16, -1 as int, every bit set in a bitmap -- so that a read before the kernel's
+// own write changes the results.  Called by every thread before any other LDS access.
+__device__ __forceinline__ void poison_lds(void* p, unsigned bytes) {
+  uint32_t* w = static_cast<uint32_t*>(p);
+  for (unsigned i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+}
+
 // Flat workgroup id remapped so that consecutive logical ids land on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8); logical id
 // w = xcd * per_xcd + slot keeps neighbours (which share data) in one L2.
@@ -138,4 +146,9 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 namespace dsa_host {
 dsa_status fail(dsa_status st, const char* fmt, ...);
 dsa_status check_launch(const char* what);
+// DSA_DEBUG_POISON=1 in the environment: kernels poison their LDS before use and the library's
+// written-before-read workspace regions are filled with all-one bytes before each call (a debug
+// mode for eager calls; its fill kernels are not meant for graph capture)
+bool debug_poison();
+void poison_fill(void* p, size_t bytes, hipStream_t s);
 }  // namespace dsa_host

@@ -31,6 +31,7 @@ struct IdxArgs {
   const uint8_t* k_cache; const void* k_scale;
   float* scores; int32_t* dots; long ld;
   uint32_t* hist; int hist_k;            // optional top-k digit histogram [T][kHistShards][kHistBins]
+  int poison;                            // debug: poison LDS before use
   int H; int ngrp; int scale_f16; int B; int T;
   const int32_t* bt; int bps; int bs_log2;   // paged caches: block table (NULL: flat rows)
 };
@@ -149,6 +150,11 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   constexpr int QR = SEPQ ? (QB > G * kCK * 4 ? QB : G * kCK * 4) : 0;
   __shared__ __attribute__((aligned(1024))) unsigned char kl[KB + QR];
   __shared__ float scl_s[(DOTS || SEPQ) ? 1 : G][kCK];
+  if (a.poison) {
+    poison_lds(&kl, sizeof(kl));
+    poison_lds(&scl_s, sizeof(scl_s));
+    __syncthreads();
+  }
   float (*scl)[kCK] = SEPQ ? reinterpret_cast<float (*)[kCK]>(kl + KB) : scl_s;   // scores of the chunk
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -507,6 +513,11 @@ __global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
   constexpr int H = 64, D = 128;
   __shared__ __attribute__((aligned(16))) uint8_t qs[kPT * H * D];       // 128 KiB
   __shared__ __attribute__((aligned(16))) float wq[kPT][H];
+  if (a.poison) {
+    poison_lds(&qs, sizeof(qs));
+    poison_lds(&wq, sizeof(wq));
+    __syncthreads();
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hv = lane >> 5, col = lane & 31;
   const int b = blockIdx.y;
@@ -826,6 +837,21 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
   __shared__ float newks[PG];                                                    // ... and scales
   __shared__ __attribute__((aligned(16))) float ptab[PRO ? 2 * G * 64 : 4];      // cos, sin rows
   __shared__ __attribute__((aligned(16))) unsigned char nkraw[PRO ? G * D * 4 : 16];   // raw new keys
+  if (sa.a.poison) {
+    poison_lds(&ring, sizeof(ring));
+    poison_lds(&qsm, sizeof(qsm));
+    poison_lds(&scl, sizeof(scl));
+    poison_lds(&wraw, sizeof(wraw));
+    poison_lds(&sraw, sizeof(sraw));
+    poison_lds(&wqt, sizeof(wqt));
+    poison_lds(&sbt, sizeof(sbt));
+    poison_lds(&qsc, sizeof(qsc));
+    poison_lds(&newk, sizeof(newk));
+    poison_lds(&newks, sizeof(newks));
+    poison_lds(&ptab, sizeof(ptab));
+    poison_lds(&nkraw, sizeof(nkraw));
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hv = lane >> 5, col = lane & 31;
@@ -1322,6 +1348,7 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.q_codes = (const uint8_t*)q; a.q_scale = qs; a.w = (const dsa::u16*)w;
   a.k_cache = (const uint8_t*)k; a.k_scale = ks; a.scores = scores; a.dots = dots; a.ld = ld;
   a.hist = hist; a.hist_k = hist_k;
+  a.poison = dsa_host::debug_poison();
   a.H = H; a.scale_f16 = sdt == DSA_F16; a.B = bt->num_seqs; a.T = bt->num_q;
   if (pg) { a.bt = pg->block_table; a.bps = pg->blocks_per_seq; a.bs_log2 = bs_log2; }
   const int G = bt->max_q_per_seq >= 3 ? 4 : bt->max_q_per_seq;

@@ -51,6 +51,7 @@ struct SfaArgs {
   u16* out; u16* ws_o; float* ws_ml;
   int T, B, Hq, n_hg, n_split, kps;
   const int32_t* bt; int bps; int bs_log2;   // paged cache: block table (NULL: flat rows)
+  int poison;                                // debug: poison LDS before use
 };
 constexpr int kMaxBps = 2048;                        // paged: block-table entries per sequence
 
@@ -231,6 +232,14 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   __shared__ float abuf[2][NH];
   __shared__ float fin[2][NH];
   __shared__ __attribute__((aligned(16))) int sidx[kMaxKps];
+  if (a.poison) {
+    poison_lds(&ring, sizeof(ring));
+    poison_lds(&pbuf, sizeof(pbuf));
+    poison_lds(&abuf, sizeof(abuf));
+    poison_lds(&fin, sizeof(fin));
+    poison_lds(&sidx, sizeof(sidx));
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
@@ -626,6 +635,7 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   a.scale_log2 = scale * dsa::kLog2e; a.out = (dsa::u16*)out;
   a.T = bt->num_q; a.B = bt->num_seqs; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
   if (pg) { a.bt = pg->block_table; a.bps = pg->blocks_per_seq; a.bs_log2 = bs_log2; }
+  a.poison = dsa_host::debug_poison();
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
     a.ws_o = (dsa::u16*)ws;
@@ -638,6 +648,11 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
 
 static void sfa_launch_split(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)((long)a.T * p.n_hg * p.n_split));
+  if (a.poison && p.n_split > 1) {                       // split partials: written before merged
+    const size_t n = (size_t)a.T * p.n_split * a.Hq;
+    dsa_host::poison_fill(a.ws_o, n * dsa::kDv * 2, s);
+    dsa_host::poison_fill(a.ws_ml, n * 2 * 4, s);
+  }
   if (p.n_split == 1) hipLaunchKernelGGL((dsa::sfa_kernel<true>), grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL((dsa::sfa_kernel<false>), grid, dim3(512), 0, s, a);
 }

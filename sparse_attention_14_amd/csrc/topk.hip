@@ -55,6 +55,7 @@ constexpr int kRowMinT = 256;        // batches of at least this many rows take 
 struct TkArgs {
   const int32_t* q_pos; const float* scores; long ld; int k; int T; int nch;
   int32_t* idx; uint32_t* hist; uint32_t* bg; uint32_t* cnt; uint32_t* bits; uint64_t* slots;
+  int poison;                        // debug: poison LDS before use
 };
 
 // Keeps the loads issued above it in place: the compiler would otherwise sink loads that only
@@ -73,6 +74,10 @@ __device__ __forceinline__ float4 load4(const float* row, long ld, int ch) {
 // chunk in LDS; non-zero bins are added to shard (chunk % kShards) of the row's.
 __global__ void __launch_bounds__(kNT) topk_hist(TkArgs a) {
   __shared__ uint32_t h[kBins];
+  if (a.poison) {
+    poison_lds(&h, sizeof(h));
+    __syncthreads();
+  }
   const int t = blockIdx.y, ch = blockIdx.x;
   const int p = a.q_pos[t];
   const float4 v = load4(a.scores + (long)t * a.ld, a.ld, ch);
@@ -99,6 +104,13 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
   __shared__ uint32_t sh[kNT / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t bw[kCW];
+  if (a.poison) {
+    poison_lds(&h, sizeof(h));
+    poison_lds(&sh, sizeof(sh));
+    poison_lds(&res, sizeof(res));
+    poison_lds(&bw, sizeof(bw));
+    __syncthreads();
+  }
   const int t = blockIdx.y, ch = blockIdx.x;
   const int tid = threadIdx.x;
   const int p = a.q_pos[t];
@@ -185,6 +197,17 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   __shared__ uint32_t bw[kCW];
   __shared__ uint32_t tw[kCW];
   __shared__ uint32_t red[4];
+  if (a.poison) {
+    poison_lds(&h, sizeof(h));
+    poison_lds(&sh, sizeof(sh));
+    poison_lds(&res, sizeof(res));
+    poison_lds(&scnt, sizeof(scnt));
+    poison_lds(&flag, sizeof(flag));
+    poison_lds(&bw, sizeof(bw));
+    poison_lds(&tw, sizeof(tw));
+    poison_lds(&red, sizeof(red));
+    __syncthreads();
+  }
   const int t = blockIdx.y, ch = blockIdx.x;
   const int tid = threadIdx.x;
   const int nch_m = a.nch;
@@ -387,6 +410,14 @@ __global__ void __launch_bounds__(kRNT) topk_row(TkArgs a) {
   __shared__ uint32_t tbl[kQJ * kRNW + 1];
   __shared__ uint32_t sh[kRNT / 64];
   __shared__ uint32_t res[2];
+  if (a.poison) {
+    poison_lds(&lst, sizeof(lst));
+    poison_lds(&h, sizeof(h));
+    poison_lds(&tbl, sizeof(tbl));
+    poison_lds(&sh, sizeof(sh));
+    poison_lds(&res, sizeof(res));
+    __syncthreads();
+  }
   const int t = blockIdx.x, tid = threadIdx.x;
   const int k = a.k;
   const float* row = a.scores + (long)t * a.ld;
@@ -657,6 +688,7 @@ static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t
   dsa::TkArgs a{};
   a.q_pos = bt->q_pos; a.scores = scores; a.ld = ld; a.k = k; a.T = bt->num_q; a.idx = idx;
   a.nch = tk_nch(bt->max_kv_len);
+  a.poison = dsa_host::debug_poison();
   char* w = (char*)ws;
   char* o = w + ((ws_bytes - L.others) & ~(size_t)255);   // >= w + L.hist
   a.hist = (uint32_t*)w;
@@ -671,6 +703,8 @@ static dsa_status topk_prepare(const dsa_batch* bt, const float* scores, int64_t
 // Select + finalize (the row histograms are already in the workspace).
 static void topk_tail(const dsa::TkArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.nch, (unsigned)a.T);
+  if (a.poison)                                          // written by select before finalize reads
+    dsa_host::poison_fill(a.bg, (size_t)((const char*)(a.slots + (size_t)a.T * a.nch * dsa::kCap) - (const char*)a.bg), s);
   hipLaunchKernelGGL(dsa::topk_select, grid, dim3(dsa::kNT), 0, s, a);
   hipLaunchKernelGGL(dsa::topk_finalize, grid, dim3(dsa::kNT), 0, s, a);
 }
