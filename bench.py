@@ -165,6 +165,12 @@ def main():
                            scale=wl.scale, buf=s.buf, q_cos=d0["q_cos"], q_sin=d0["q_sin"],
                            k_cos=new_cos, k_sin=new_sin)
 
+    def step_separate(s):
+        return decode_step(batch, cfg, q_in=s.q_in, k_in=s.k_in, new_slots=new_slots, w=s.w,
+                           k_cache=s.k_cache, k_scale=s.k_scale, q_attn=s.q, kv=s.kv, sink=sink,
+                           scale=wl.scale, buf=s.buf, q_cos=d0["q_cos"], q_sin=d0["q_sin"],
+                           k_cos=new_cos, k_sin=new_sin, fused=False)
+
     # stage launchers (for per-kernel timing)
     def st_prolog(s):
         dsa.dsa_indexer_prolog(H, D, cfg.code, cfg.scale_dt, q_in=s.q_in, q_cos=d0["q_cos"],
@@ -191,6 +197,13 @@ def main():
         dsa.dsa_indexer_topk(batch, H, D, cfg.code, cfg.scale_dt, s.buf.q_codes, s.buf.q_scale,
                              s.w, s.k_cache, s.k_scale, k, scores=s.buf.scores, idx=s.buf.idx,
                              ws=s.buf.ws_topk)
+
+    def st_indexer_attention(s):
+        dsa.dsa_indexer_attention(batch, H, D, cfg.code, cfg.scale_dt, q_codes=s.buf.q_codes,
+                                  q_scale=s.buf.q_scale, w=s.w, k_cache=s.k_cache,
+                                  k_scale=s.k_scale, k=k, q=s.q, kv=s.kv, sink=sink,
+                                  scale=wl.scale, scores=s.buf.scores, idx=s.buf.idx,
+                                  out=s.buf.out, ws=s.buf.ws_dia)
 
     def st_sfa(s):
         dsa.dsa_sparse_attn_decode(batch, s.q, s.kv, s.buf.idx, sink, wl.scale, out=s.buf.out,
@@ -321,8 +334,9 @@ def main():
         if e.status != DSA_ERR_UNSUPPORTED:
             raise
         fused_stage = {}
-    stages = {"prolog": st_prolog, "indexer": st_indexer, "indexer_topk": st_indexer_topk,
-              **fused_stage,
+    stages = {"step_separate_calls": step_separate,
+              "prolog": st_prolog, "indexer": st_indexer, "indexer_topk": st_indexer_topk,
+              **fused_stage, "indexer_attention": st_indexer_attention,
               "sfa": st_sfa, "sfa_split": st_sfa_split, "sfa_merge": st_sfa_merge,
               "indexer_topk_paged": st_indexer_topk_paged, "sfa_paged": st_sfa_paged}
     stage_us = {}

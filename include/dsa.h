@@ -333,6 +333,63 @@ dsa_status dsa_sparse_attn_decode_noalloc(const dsa_batch* batch, int32_t Hq, co
                                           const int32_t* idx, int32_t k, const float* sink,
                                           float scale, void* out, void* stream);
 
+/* ---------------------------------------------------------------- indexer attention ------- */
+/*
+ * [DIA] "Deepseek Indexer Attention": the indexer prolog, the Lightning Indexer, its TopK and
+ * the Sparse Flash Attention of a decode step back to back, in one call.  The results equal
+ *   dsa_indexer_prolog_topk(prolog, batch, q_in, q_cos, q_sin, k_in, w, q_codes, q_scale,
+ *                           k_cache, k_scale, k, scores, ld, idx, ...)      when prolog != NULL
+ *   dsa_indexer_topk(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
+ *                    k_scale, scores, ld, k, idx, ...)                     when prolog == NULL
+ * followed by
+ *   dsa_sparse_attn_decode(batch, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ...)
+ * with the argument meanings, layouts and errors of those calls (flat caches only).  With a
+ * prolog, H, D, code_dtype and scale_dtype must equal the prolog's.  Every argument is checked
+ * before the first launch.
+ * Schedule (chosen from the shapes; the results are identical): for at most 16 query tokens on
+ * rows of at most 65536 positions the attention workgroups resolve their own slice of the
+ * selection from the state the top-k's select pass leaves in the workspace (the k-th key of the
+ * row by two more radix digits over the candidates, then their slots of the ascending
+ * selection), which takes the top-k's separate finalize launch out of the step; idx is written
+ * by those workgroups.  Other decode batches run the finalize pass before the attention, and
+ * batches of 256 or more tokens the row top-k.  DSA_DIA_SCHEDULE=slice|finalize overrides the
+ * choice below 256 tokens (testing).
+ *   ws: device workspace of at least dsa_indexer_attention_workspace_size(T, max_kv_len, k, Hq)
+ *       bytes, 256-byte aligned, with the contract of the top-k workspace (zero-filled before
+ *       its first use, left so by every call; sized for the largest num_q and max_kv_len of the
+ *       calls that share it; calls sharing it must not overlap).
+ */
+typedef struct dsa_dia {
+  const dsa_prolog_cfg* prolog;  /* NULL: q_codes, q_scale and the batch's new key rows are   */
+                                 /* already quantized inputs                                */
+  const void* q_in;              /* prolog only: device [T, H, D] in_dtype                   */
+  const float* q_cos;            /* prolog with rope_dim > 0: device [T, rope_dim / 2] fp32  */
+  const float* q_sin;
+  const void* k_in;              /* prolog only: device [T, D] in_dtype, token t's new key    */
+                                 /* row (written at kv_start[seq(t)] + q_pos[t])              */
+  int32_t H, D;                  /* indexer heads and head dim                               */
+  dsa_dtype code_dtype, scale_dtype;
+  void* q_codes;                 /* device [T, H, D] codes (written by the prolog)            */
+  void* q_scale;                 /* device [T, H] (written by the prolog)                     */
+  const void* w;                 /* device [T, H] fp16 head weights                           */
+  void* k_cache;                 /* device [N, D] key codes                                   */
+  void* k_scale;                 /* device [N] key scales                                     */
+  float* scores;                 /* device [T, ld] fp32 indexer scores (output)               */
+  int64_t ld;
+  int32_t k;                     /* top-k size, 1 .. 2048                                     */
+  int32_t* idx;                  /* device [T, k] int32 selection (output)                    */
+  int32_t Hq;                    /* attention heads, 16 or 128                                */
+  const void* q;                 /* device [T, Hq, 576] bf16                                  */
+  const void* kv;                /* device latent rows of 576 bf16                            */
+  int64_t kv_row_stride;
+  const float* sink;             /* device [Hq] fp32, or NULL                                 */
+  float scale;
+  void* out;                     /* device [T, Hq, 512] bf16 (output)                         */
+} dsa_dia;
+size_t dsa_indexer_attention_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k, int32_t Hq);
+dsa_status dsa_indexer_attention(const dsa_batch* batch, const dsa_dia* args, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- paged caches ----------- */
 /*
  * [LI] the Page Attention layout of the caches: a sequence's rows are stored in fixed-size

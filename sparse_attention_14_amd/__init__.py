@@ -11,7 +11,8 @@ import importlib
 
 _EXPORTS = ("Batch", "make_batch", "dsa_indexer_prolog", "dsa_indexer_scores",
             "dsa_indexer_dots_i32", "dsa_e4m3_dots", "dsa_indexer_prolog_topk", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_attn_decode",
-            "dsa_sparse_attn_workspace_size", "dsa_last_error", "dsa_version")
+            "dsa_sparse_attn_workspace_size", "dsa_indexer_attention",
+            "dsa_indexer_attention_workspace_size", "dsa_last_error", "dsa_version")
 
 __all__ = ["dsa", *_EXPORTS]
 

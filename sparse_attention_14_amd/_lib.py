@@ -57,6 +57,18 @@ class DsaProjections(ctypes.Structure):
                 ("q_pre", ctypes.c_void_p), ("k_pre", ctypes.c_void_p), ("weight", ctypes.c_void_p)]
 
 
+class DsaDia(ctypes.Structure):
+    _fields_ = [("prolog", ctypes.POINTER(DsaPrologCfg)), ("q_in", ctypes.c_void_p),
+                ("q_cos", ctypes.c_void_p), ("q_sin", ctypes.c_void_p), ("k_in", ctypes.c_void_p),
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("code_dtype", ctypes.c_int),
+                ("scale_dtype", ctypes.c_int), ("q_codes", ctypes.c_void_p),
+                ("q_scale", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("ld", ctypes.c_int64),
+                ("k", ctypes.c_int32), ("idx", ctypes.c_void_p), ("Hq", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_row_stride", ctypes.c_int64),
+                ("sink", ctypes.c_void_p), ("scale", ctypes.c_float), ("out", ctypes.c_void_p)]
+
+
 SIGNATURES = {
     "dsa_indexer_prolog": (ctypes.c_int, [ctypes.POINTER(DsaPrologCfg), _I32, _P, _P, _P, _P, _P,
                                           _I32, _P, _P, _P, _P, _P, _P, _P]),
@@ -84,6 +96,8 @@ SIGNATURES = {
                                               _P, _P, _P, _P, _P, _P, _I64, _I32, _P, _P, _SZ, _P]),
     "dsa_sparse_attn_decode_paged": (ctypes.c_int, [_BP, _PP, _I32, _P, _P, _I64, _P, _I32, _P,
                                                     ctypes.c_float, _P, _P, _SZ, _P]),
+    "dsa_indexer_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "dsa_indexer_attention": (ctypes.c_int, [_BP, ctypes.POINTER(DsaDia), _P, _SZ, _P]),
     "dsa_indexer_projections_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "dsa_indexer_projections": (ctypes.c_int, [ctypes.POINTER(DsaProjections), _P, _SZ, _P]),
     "dsa_last_error": (ctypes.c_char_p, []),

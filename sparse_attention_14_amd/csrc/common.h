@@ -69,6 +69,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 constexpr int kHistBins = 2048;          // top-k radix histogram: the top 11 bits of the key
 constexpr int kHistShards = 4;           // copies of each row histogram (spread atomic traffic)
+// The top-k select pass's per-row state in its workspace, read by the finalize pass and by the
+// attention kernel that resolves its own slice of the selection: per chunk of kTkChunk scores,
+// the count above the threshold digit and of candidates, a position bitmap and kTkCap
+// candidate slots (key << 32 | position).
+constexpr int kTkChunk = 4096;           // scores per chunk
+constexpr int kTkCW = kTkChunk / 32;     // bitmap words per chunk
+constexpr int kTkCap = 512;              // candidate slots per chunk
+constexpr int kTkLoad = 4096;            // candidate entries of a row read in the first trip
 
 // Inclusive prefix sum over the 64 lanes of a wave: four row shifts within each 16-lane row,
 // then the row broadcasts of lanes 15 and 31 (DPP, no LDS round trip).
@@ -82,14 +90,22 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// A workgroup barrier: __syncthreads(), or with LDS_ONLY a barrier that orders LDS traffic only
+// (it does not wait for global loads in flight, e.g. direct-to-LDS DMA issued earlier).
+template <bool LDS_ONLY>
+__device__ __forceinline__ void block_barrier() {
+  if constexpr (LDS_ONLY) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __syncthreads();
+}
+
 // Exclusive prefix sum over the NT threads of the block (one barrier); `total` gets the sum.
 // sh holds NT/64 words; consecutive uses of one sh must be separated by a barrier.
-template <int NT>
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) sh[w] = inc;
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
@@ -103,7 +119,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
 
 // The digit holding the need-th largest element of an LDS histogram over kBins digits:
 // res[0] = digit, res[1] = elements in larger digits.  Ends with a barrier.
-template <int NT>
+template <int NT, bool LDS_ONLY = false>
 __device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t* res) {
   constexpr int PER = kHistBins / NT;
   const int tid = threadIdx.x;
@@ -112,13 +128,13 @@ __device__ void find_digit_desc(const uint32_t* hist, uint32_t need, uint32_t* s
 #pragma unroll
   for (int j = 0; j < PER; ++j) { loc[j] = hist[kHistBins - 1 - (tid * PER + j)]; tot += loc[j]; }
   uint32_t all;
-  uint32_t before = block_excl_scan<NT>(tot, sh, all);
+  uint32_t before = block_excl_scan<NT, LDS_ONLY>(tot, sh, all);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (before < need && need <= before + loc[j]) { res[0] = kHistBins - 1 - (tid * PER + j); res[1] = before; }
     before += loc[j];
   }
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
 }
 
 // Debug poisoning (DSA_DEBUG_POISON=1, race detection): fill an LDS object with all-one bytes --
@@ -151,4 +167,12 @@ dsa_status check_launch(const char* what);
 // mode for eager calls; its fill kernels are not meant for graph capture)
 bool debug_poison();
 void poison_fill(void* p, size_t bytes, hipStream_t s);
+// A selection still pending in the top-k workspace after the select pass (per-row threshold
+// digit, per-chunk counts, bitmaps and candidate slots, the digit histograms), resolved by the
+// attention kernel itself; idx receives the selection.  See sfa.hip / topk.hip.
+struct SfaSel {
+  const float* scores; long ld;
+  const uint32_t* bg; const uint32_t* cnt; const uint32_t* bits; const uint64_t* slots;
+  uint32_t* hist; int nch; int32_t* idx;
+};
 }  // namespace dsa_host

@@ -1355,9 +1355,6 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
   a.ngrp = (bt->max_q_per_seq + G - 1) / G;
   const long gy = (long)bt->num_seqs * a.ngrp;
   if (gy > 65535L) return fail(DSA_ERR_INVALID_ARG, "%s: too many token groups", fn);
-  if (validate_only) return DSA_OK;
-  hipStream_t s = (hipStream_t)stream;
-  const bool fp8 = code == DSA_FP8_E4M3;
   // only the streaming kernel accumulates the top-k's histogram (decode groups)
   if (hist && a.ngrp != 1) return fail(DSA_ERR_UNSUPPORTED, "%s: fused histogram needs at most 4 tokens per sequence", fn);
   if (pro) {
@@ -1368,6 +1365,9 @@ static dsa_status indexer_common(const dsa_batch* bt, int H, int D, dsa_dtype co
       return fail(DSA_ERR_UNSUPPORTED, "%s: %d query tokens per sequence of %s rows exceed the in-kernel staging (%ld > %d bytes)",
                   fn, bt->max_q_per_seq, pro->in_bf16 ? "bf16" : "fp32", rbytes, dsa::pro_capacity(G, D));
   }
+  if (validate_only) return DSA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool fp8 = code == DSA_FP8_E4M3;
   if (a.ngrp == 1) {
     // decode: the streaming kernel, spans (multiples of 256 keys) sized for about one
     // workgroup per CU
@@ -1444,9 +1444,11 @@ dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D,
                                    dsa_dtype scale_dtype, const void* q_codes, const void* q_scale,
                                    const void* w, const void* k_cache, const void* k_scale,
                                    float* scores, int64_t ld, uint32_t* hist, int32_t k,
-                                   void* stream, const char* fn, const dsa_paging* paging) {
+                                   void* stream, const char* fn, const dsa_paging* paging,
+                                   bool validate_only) {
   return indexer_common(batch, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
-                        k_scale, scores, nullptr, false, ld, hist, k, stream, fn, paging);
+                        k_scale, scores, nullptr, false, ld, hist, k, stream, fn, paging, nullptr,
+                        validate_only);
 }
 
 dsa_status dsa_prolog_own_keys(const dsa_prolog_cfg* cfg, const dsa_batch* bt, const void* q_in,
@@ -1465,7 +1467,8 @@ dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_b
                                           const void* q_in, const float* q_cos, const float* q_sin,
                                           const void* k_in, const void* w, void* q_codes, void* q_scale,
                                           void* k_cache, void* k_scale, float* scores, int64_t ld,
-                                          uint32_t* hist, int32_t k, void* stream, const char* fn) {
+                                          uint32_t* hist, int32_t k, void* stream, const char* fn,
+                                          bool validate_only) {
   dsa_status st = check_batch(batch, fn);
   if (st != DSA_OK || batch->num_q == 0) return st;
   if (!q_in || !k_in || !q_codes || !q_scale || !k_cache || !k_scale)
@@ -1496,7 +1499,7 @@ dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_b
     st = indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
                         k_cache, k_scale, scores, nullptr, false, ld, hist, k, nullptr, fn, nullptr,
                         nullptr, /*validate_only=*/true);
-    if (st != DSA_OK) return st;
+    if (st != DSA_OK || validate_only) return st;
     st = dsa_prolog_own_keys(cfg, batch, q_in, q_cos, q_sin, q_codes, q_scale, k_in, k_cache, k_scale, stream);
     if (st != DSA_OK) return st;
     return indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
@@ -1508,7 +1511,8 @@ dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_b
   p.in_bf16 = cfg->in_dtype == DSA_BF16; p.rope_dim = cfg->rope_dim; p.rope_offset = cfg->rope_offset;
   p.rope_interleaved = cfg->rope_interleaved; p.hadamard = cfg->hadamard; p.round_scale = cfg->round_scale;
   return indexer_common(batch, cfg->H, cfg->D, cfg->code_dtype, cfg->scale_dtype, q_codes, q_scale, w,
-                        k_cache, k_scale, scores, nullptr, false, ld, hist, k, stream, fn, nullptr, &p);
+                        k_cache, k_scale, scores, nullptr, false, ld, hist, k, stream, fn, nullptr, &p,
+                        validate_only);
 }
 
 extern "C" dsa_status dsa_indexer_dots_i32(const dsa_batch* batch, int32_t H, int32_t D,

@@ -52,6 +52,13 @@ struct SfaArgs {
   int T, B, Hq, n_hg, n_split, kps;
   const int32_t* bt; int bps; int bs_log2;   // paged cache: block table (NULL: flat rows)
   int poison;                                // debug: poison LDS before use
+  // selection resolved by the kernel itself (sfa_kernel<., true>) from the top-k select pass's
+  // state: the rows' scores (overflow rows re-read them), query positions, the per-row
+  // threshold digit and count above it, per-chunk counts, bitmaps and candidate slots, the
+  // digit histograms (zeroed here for the next call) and the index output (may be NULL)
+  const int32_t* q_pos; const float* scores; long ld;
+  const uint32_t* tk_bg; const uint32_t* tk_cnt; const uint32_t* tk_bits; const uint64_t* tk_slots;
+  uint32_t* tk_hist; int tk_nch; int32_t* idx_out;
 };
 constexpr int kMaxBps = 2048;                        // paged: block-table entries per sequence
 
@@ -221,10 +228,217 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
   }
 }
 
+// The selection of token t in ascending position order, slots [kbeg, kbeg + nkeys) of it, into
+// sidx (padded with -1 to nkeys_pad), resolved from what the select pass left in the top-k
+// workspace: the threshold digit b1 of the row (the top 11 bits of the k-th largest key), the
+// count G of keys above it, per 4096-position chunk the bitmap of positions above b1 and the
+// candidates with digit b1.  Two more radix digits over the candidates give the exact k-th
+// key K*; the selection is then the bitmap, the candidates above K* and the lowest-position
+// ties at K* ([LI] "Lightning Indexer": the indexer's TopK keeps the k highest scores; ties to
+// the lower position, the rule of the separate top-k call).  Every workgroup of the token
+// computes the same K* (no hand-over between workgroups).
+//
+// slice_loads issues the one memory round trip (before the workgroup's Q loads, so that waiting
+// for it does not wait for them); select_slice then works in LDS only, with LDS-only barriers.
+// `scr` is LDS scratch: 2 x 32 KiB of row bitmaps and 9 KiB of histogram and counters.  Rows
+// whose candidate lists overflow the first trip re-read the row's scores.  The slice ends in
+// sidx, not yet behind a barrier.
+constexpr int kSelNT = 512;                            // threads of the attention workgroup
+constexpr int kSelLoad = kTkLoad / kSelNT;             // first-trip candidate entries per thread
+constexpr int kSelG = 4;                               // 16-byte bitmap groups per thread (<= 64 chunks)
+struct SliceIn {
+  int p, sl, gpt;
+  uint32_t b1, G, my_cnt;
+  uint64_t ev[kSelLoad];
+  uint4 wv[kSelG];
+};
+
+__device__ __forceinline__ SliceIn slice_loads(const SfaArgs& a, int t) {
+  const int tid = threadIdx.x, nch_m = a.tk_nch;
+  SliceIn in;
+  in.p = a.q_pos[t];
+  in.b1 = a.tk_bg[2 * t];
+  in.G = a.tk_bg[2 * t + 1];
+  in.my_cnt = a.tk_cnt[(long)t * nch_m + min(tid, nch_m - 1)];   // masked later
+  // first-trip candidate entries: entry f of the row's lists is chunk f >> sl, slot f & (2^sl - 1)
+  in.sl = min(31 - __clz(kTkLoad / nch_m), 9);         // kTkCap = 512
+  const uint64_t* srow = a.tk_slots + (long)t * nch_m * kTkCap;
+#pragma unroll
+  for (int u = 0; u < kSelLoad; ++u) {
+    const int f = tid + u * kSelNT;
+    in.ev[u] = srow[(long)min(f >> in.sl, nch_m - 1) * kTkCap + (f & ((1 << in.sl) - 1))];
+  }
+  // this thread's bitmap words: 16-byte groups gpt * tid .. + gpt - 1 (position order)
+  const int ngr = nch_m * kTkCW / 4;
+  in.gpt = (ngr + kSelNT - 1) / kSelNT;
+  const uint4* brow = reinterpret_cast<const uint4*>(a.tk_bits + (long)t * nch_m * kTkCW);
+#pragma unroll
+  for (int j = 0; j < kSelG; ++j) {
+    const int gi = in.gpt * tid + j;
+    const bool own = j < in.gpt && gi < ngr;
+    const uint4 v = brow[own ? gi : 0];                // any valid group, masked
+    const uint32_t m = own ? 0xFFFFFFFFu : 0u;
+    in.wv[j] = uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+  }
+  return in;
+}
+
+__device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in, int t, int kbeg, int nkeys,
+                             int nkeys_pad, unsigned char* scr, int* sidx, bool write_idx,
+                             bool zero_hist) {
+  constexpr int NT = kSelNT;
+  const int tid = threadIdx.x;
+  const int k = a.k, nch_m = a.tk_nch, p = in.p, sl = in.sl, gpt = in.gpt;
+  if (p + 1 <= k) {                                    // short row: every visible position, then -1
+    for (int j = tid; j < nkeys_pad; j += NT) {
+      const int r = kbeg + j, v = (j < nkeys && r <= p) ? r : -1;
+      sidx[j] = v;
+      if (write_idx && j < nkeys) a.idx_out[(long)t * k + r] = v;
+    }
+    return;
+  }
+  if (zero_hist) {                                     // read by the select pass only
+    uint32_t* gh = a.tk_hist + (long)t * kHistShards * kHistBins;
+    for (int i = tid; i < kHistShards * kHistBins; i += NT) gh[i] = 0u;
+  }
+  const int nch = p / kTkChunk + 1;                    // chunks of this row (later ones are stale)
+  const int ngr = nch_m * kTkCW / 4, gvalid = nch * kTkCW / 4;
+  uint4* sel = reinterpret_cast<uint4*>(scr);          // [64 * kTkCW / 4] selection bitmap
+  uint4* tie = sel + 64 * kTkCW / 4;                   // [64 * kTkCW / 4] positions with key K*
+  uint32_t* h = reinterpret_cast<uint32_t*>(tie + 64 * kTkCW / 4);   // [kHistBins]
+  uint32_t* sh = h + kHistBins;                        // [NT / 64]
+  uint32_t* res = sh + NT / 64;                        // [2]
+  uint32_t* flag = res + 2;                            // [1]
+  uint32_t* scnt = flag + 2;                           // [64]
+  for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
+  if (tid < 64) scnt[tid] = tid < nch ? in.my_cnt : 0u;   // tid < nch <= nch_m
+  if (tid == 0) *flag = 0u;
+  // selects below are written as masks: a select between two arrays becomes a select of
+  // addresses, which puts both in scratch memory
+  auto masked = [](uint4 v, bool keep) {
+    const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+    return uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+  };
+#pragma unroll
+  for (int j = 0; j < kSelG; ++j) {
+    const int gi = gpt * tid + j;
+    if (j < gpt && gi < ngr) { sel[gi] = masked(in.wv[j], gi < gvalid); tie[gi] = uint4{0u, 0u, 0u, 0u}; }
+  }
+  block_barrier<true>();
+  if (tid < nch && (in.my_cnt >> 16) > (1u << sl)) *flag = 1u;
+  // candidate validity without branches: every count first (chunk f >> sl <= 63; chunks past
+  // the row read 0)
+  uint32_t cn[kSelLoad];
+#pragma unroll
+  for (int u = 0; u < kSelLoad; ++u) cn[u] = scnt[(tid + u * NT) >> sl];
+  uint32_t cvalid = 0;
+#pragma unroll
+  for (int u = 0; u < kSelLoad; ++u)
+    cvalid |= (uint32_t)((uint32_t)((tid + u * NT) & ((1 << sl) - 1)) < (cn[u] >> 16)) << u;
+  block_barrier<true>();                               // flag
+  const bool streamed = *flag != 0u;
+  const uint32_t b1 = in.b1;
+  const uint32_t need = (uint32_t)k - in.G;            // 1 <= need <= #candidates
+  const float* row = a.scores + (long)t * a.ld;
+  auto each_cand = [&](auto&& fn) {
+    if (!streamed) {
+#pragma unroll
+      for (int u = 0; u < kSelLoad; ++u)
+        if ((cvalid >> u) & 1u) fn((uint32_t)(in.ev[u] >> 32), (uint32_t)in.ev[u]);
+    } else {
+      for (int c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int j = 0; j < kTkChunk / (4 * NT); ++j) {
+          const long e0 = (long)c * kTkChunk + 4 * (tid + NT * j);
+          const float4 x = *reinterpret_cast<const float4*>(row + min(e0, (a.ld & ~3L) - 4));
+          const float ff[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t key = order_key(ff[q]);
+            if (e0 + q <= p && (key >> 21) == b1) fn(key, (uint32_t)(e0 + q));
+          }
+        }
+      }
+    }
+  };
+  each_cand([&](uint32_t key, uint32_t) { atomicAdd(&h[(key >> 10) & 0x7FFu], 1u); });
+  block_barrier<true>();
+  find_digit_desc<NT, true>(h, need, sh, res);
+  const uint32_t b2 = res[0];
+  const uint32_t need2 = need - res[1];                // >= 1, among the b2 bin
+  block_barrier<true>();
+  for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
+  block_barrier<true>();
+  each_cand([&](uint32_t key, uint32_t) {
+    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h[key & 0x3FFu], 1u);
+  });
+  block_barrier<true>();
+  find_digit_desc<NT, true>(h, need2, sh, res);
+  const uint32_t kstar = (b1 << 21) | (b2 << 10) | res[0];
+  const uint32_t n_eq = h[res[0]];
+  const uint32_t take_eq = need2 - res[1];             // >= 1
+  uint32_t* selw = reinterpret_cast<uint32_t*>(sel);
+  uint32_t* tiew = reinterpret_cast<uint32_t*>(tie);
+  each_cand([&](uint32_t key, uint32_t pos) {
+    if (key > kstar) atomicOr(&selw[pos >> 5], 1u << (pos & 31));
+    else if (key == kstar) atomicOr(&tiew[pos >> 5], 1u << (pos & 31));
+  });
+  block_barrier<true>();
+  // this thread's words, in position order: the selection with the kept ties
+  uint32_t sw[4 * kSelG], tw[4 * kSelG];
+  uint32_t ntie = 0, nsel = 0;
+#pragma unroll
+  for (int j = 0; j < kSelG; ++j) {
+    const int gi = gpt * tid + j;
+    const bool own = j < gpt && gi < ngr;
+    const int gr = own ? gi : 0;                       // any valid group, masked
+    const uint4 s4 = masked(sel[gr], own), t4 = masked(tie[gr], own);
+    sw[4 * j] = s4.x; sw[4 * j + 1] = s4.y; sw[4 * j + 2] = s4.z; sw[4 * j + 3] = s4.w;
+    tw[4 * j] = t4.x; tw[4 * j + 1] = t4.y; tw[4 * j + 2] = t4.z; tw[4 * j + 3] = t4.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 4 * kSelG; ++i) ntie += (uint32_t)__popc(tw[i]);
+  if (n_eq == take_eq) {
+#pragma unroll
+    for (int i = 0; i < 4 * kSelG; ++i) sw[i] |= tw[i];
+  } else {                                             // the take_eq lowest positions at K*
+    uint32_t tt;
+    uint32_t r = block_excl_scan<NT, true>(ntie, sh, tt);
+#pragma unroll
+    for (int i = 0; i < 4 * kSelG; ++i) {
+      uint32_t m = tw[i];
+      while (m && r < take_eq) { const uint32_t lb = m & (0u - m); sw[i] |= lb; m ^= lb; ++r; }
+    }
+    block_barrier<true>();                             // sh reuse
+  }
+#pragma unroll
+  for (int i = 0; i < 4 * kSelG; ++i) nsel += (uint32_t)__popc(sw[i]);
+  uint32_t tot;
+  uint32_t o = block_excl_scan<NT, true>(nsel, sh, tot);   // rank of this thread's first position
+  const uint32_t lo = (uint32_t)kbeg, hi = (uint32_t)(kbeg + nkeys);
+  if (o < hi && o + nsel > lo) {                       // this thread holds slots of the slice
+#pragma unroll
+    for (int i = 0; i < 4 * kSelG; ++i) {
+      uint32_t word = sw[i];
+      const int base = (4 * gpt * tid + i) * 32;
+      while (word && o < hi) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        if (o >= lo) {
+          sidx[o - lo] = base + bit;
+          if (write_idx) a.idx_out[(long)t * k + o] = base + bit;
+        }
+        ++o;
+      }
+    }
+  }
+  for (int j = nkeys + tid; j < nkeys_pad; j += NT) sidx[j] = -1;
+}
+
 // One workgroup (8 waves): token t, query heads h0 .. h0+31, selected keys [kbeg, kbeg+nkeys),
 // consumed as 32-key tiles through a 4-slot LDS ring: while the score waves work on tile k and
 // the value waves on tile k - 1, tiles k + 1 and k + 2 are in flight.
-template <bool FINAL>
+template <bool FINAL, bool TK>
 __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   constexpr int NH = 32;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kNBuf * kTileB];
@@ -253,6 +467,10 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const int nkeys = min(a.k, kbeg + a.kps) - kbeg;
   const unsigned ring_base = (unsigned)(uintptr_t)(lds_u8*)ring;
 
+  // the selection's state first (fused top-k): waiting for it must not wait for Q
+  SliceIn slin;
+  if constexpr (TK) slin = slice_loads(a, t);
+  asm volatile("" ::: "memory");
   // Prologue, two memory round trips before the first MFMA:
   //  1. Q (this workgroup's 32 heads x 1152 B, laid out like a KV tile) is moved into ring slot
   //     3 with coalesced direct-to-LDS loads; the selected indices, the token's sequence and --
@@ -278,16 +496,23 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   // issued before the token's sequence id: that id goes to a scalar register, and waiting for
   // it waits for every load issued before it
   int32_t iv[kMaxKps / 512];
+  if constexpr (!TK) {
 #pragma unroll
-  for (int u = 0; u < kMaxKps / 512; ++u) {
-    const int j = tid + 512 * u;
-    iv[u] = a.idx[(long)t * a.k + kbeg + min(j, nkeys - 1)];
+    for (int u = 0; u < kMaxKps / 512; ++u) {
+      const int j = tid + 512 * u;
+      iv[u] = a.idx[(long)t * a.k + kbeg + min(j, nkeys - 1)];
+    }
   }
   const long kv_lane = a.bt ? 0 : a.kv_start[min(lane, a.B - 1)];
   asm volatile("" ::: "memory");                       // keep the loads above issued here
   const int seq = a.q_seq[t];
   const int nkeys_pad = (nkeys + kKT - 1) / kKT * kKT;
-  if (a.bt) {
+  if constexpr (TK) {
+    // the slice of the selection (flat caches only); ring slots 0-2 are free until the first
+    // tiles are issued after the barrier below
+    select_slice(a, slin, t, kbeg, nkeys, nkeys_pad, ring, sidx, hg == 0 && a.idx_out,
+                 hg == 0 && split == 0);
+  } else if (a.bt) {
     // Paged cache: the sequence's block table goes through ring slot 2 (free until tile 2 is
     // issued) and the selected positions become cache rows before they are staged.
     int32_t bv[kMaxBps / 512];
@@ -311,10 +536,12 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
         iv[u] = (sbt[min(ix >> a.bs_log2, a.bps - 1)] << a.bs_log2) | (ix & bmask);
     }
   }
+  if constexpr (!TK) {
 #pragma unroll
-  for (int u = 0; u < kMaxKps / 512; ++u) {
-    const int j = tid + 512 * u;
-    if (j < nkeys_pad) sidx[j] = j < nkeys ? iv[u] : -1;
+    for (int u = 0; u < kMaxKps / 512; ++u) {
+      const int j = tid + 512 * u;
+      if (j < nkeys_pad) sidx[j] = j < nkeys ? iv[u] : -1;
+    }
   }
   long kv0;
   if (a.bt) {
@@ -604,7 +831,7 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
                               int64_t kv_row_stride, const int32_t* idx, int32_t k,
                               const float* sink, float scale, void* out, void* ws, size_t ws_bytes,
                               const char* fn, dsa::SfaArgs* args, dsa::SfaPlan* plan,
-                              const dsa_paging* pg = nullptr) {
+                              const dsa_paging* pg = nullptr, const dsa_host::SfaSel* sel = nullptr) {
   dsa_status st = pg ? dsa_check_batch_paged(bt, fn) : dsa_check_batch(bt, fn);
   if (st != DSA_OK) return st;
   int bs_log2 = 0;
@@ -619,7 +846,9 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   if (kv_row_stride < dsa::kDqk || kv_row_stride % 8) return fail(DSA_ERR_INVALID_ARG, "%s: kv_row_stride must be >= 576 and a multiple of 8", fn);
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (bt->num_q == 0) return DSA_OK;
-  if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "%s: a data pointer is NULL", fn);
+  if (!q || !kv || !(idx || sel) || !out) return fail(DSA_ERR_INVALID_ARG, "%s: a data pointer is NULL", fn);
+  if (sel && (pg || !sel->scores || sel->nch < 1 || sel->nch > 64))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: a pending selection needs flat caches and rows of at most 64 chunks", fn);
   if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)out) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q/kv/out must be 16-byte aligned", fn);
   const dsa::SfaPlan p = dsa::plan(bt->num_q, Hq, k);
   const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
@@ -636,6 +865,11 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   a.T = bt->num_q; a.B = bt->num_seqs; a.Hq = Hq; a.n_hg = p.n_hg; a.n_split = p.n_split; a.kps = p.kps;
   if (pg) { a.bt = pg->block_table; a.bps = pg->blocks_per_seq; a.bs_log2 = bs_log2; }
   a.poison = dsa_host::debug_poison();
+  if (sel) {
+    a.idx = nullptr; a.q_pos = bt->q_pos; a.scores = sel->scores; a.ld = sel->ld;
+    a.tk_bg = sel->bg; a.tk_cnt = sel->cnt; a.tk_bits = sel->bits; a.tk_slots = sel->slots;
+    a.tk_hist = sel->hist; a.tk_nch = sel->nch; a.idx_out = sel->idx;
+  }
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
     a.ws_o = (dsa::u16*)ws;
@@ -653,13 +887,37 @@ static void sfa_launch_split(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipSt
     dsa_host::poison_fill(a.ws_o, n * dsa::kDv * 2, s);
     dsa_host::poison_fill(a.ws_ml, n * 2 * 4, s);
   }
-  if (p.n_split == 1) hipLaunchKernelGGL((dsa::sfa_kernel<true>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((dsa::sfa_kernel<false>), grid, dim3(512), 0, s, a);
+  const bool tk = a.tk_bg != nullptr;                    // the kernel resolves its own slice
+  if (p.n_split == 1) {
+    if (tk) hipLaunchKernelGGL((dsa::sfa_kernel<true, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((dsa::sfa_kernel<true, false>), grid, dim3(512), 0, s, a);
+  } else {
+    if (tk) hipLaunchKernelGGL((dsa::sfa_kernel<false, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((dsa::sfa_kernel<false, false>), grid, dim3(512), 0, s, a);
+  }
 }
 
 static void sfa_launch_merge(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipStream_t s) {
   if (p.n_split > 1)
     hipLaunchKernelGGL(dsa::sfa_combine, dim3((unsigned)((a.T * a.Hq + 3) / 4)), dim3(256), 0, s, a);
+}
+
+// The attention half of dsa_indexer_attention (not exported): over the selection idx, or over a
+// selection still pending in the top-k workspace (sel; the kernel resolves its own slice and
+// writes sel->idx).  validate_only: check the arguments, launch nothing.
+dsa_status dsa_sfa_internal(const dsa_batch* bt, int32_t Hq, const void* q, const void* kv,
+                            int64_t kv_row_stride, const int32_t* idx, int32_t k, const float* sink,
+                            float scale, void* out, void* ws, size_t ws_bytes,
+                            const dsa_host::SfaSel* sel, void* stream, const char* fn,
+                            bool validate_only) {
+  dsa::SfaArgs a{};
+  dsa::SfaPlan p{};
+  const dsa_status st = sfa_prepare(bt, Hq, q, kv, kv_row_stride, idx, k, sink, scale, out, ws,
+                                    ws_bytes, fn, &a, &p, nullptr, sel);
+  if (st != DSA_OK || bt->num_q == 0 || validate_only) return st;
+  sfa_launch_split(a, p, (hipStream_t)stream);
+  sfa_launch_merge(a, p, (hipStream_t)stream);
+  return DSA_OK;
 }
 
 extern "C" dsa_status dsa_sparse_attn_decode(const dsa_batch* bt, int32_t Hq, const void* q,

@@ -24,6 +24,8 @@
 // [SFA] step 2: slots past the selection are -1.  Keys: fp32 bits, sign-flipped so that
 // unsigned order equals numeric order; -0.0 is mapped to +0.0 first.
 #include <algorithm>
+#include <stdlib.h>
+#include <string.h>
 
 #include "common.h"
 
@@ -32,11 +34,12 @@ namespace dsa {
 constexpr int kBins = kHistBins;     // 11-bit digits
 constexpr int kShards = kHistShards; // copies of each row histogram (spread atomic traffic)
 constexpr int kNT = 1024;            // threads per workgroup
-constexpr int kChunk = 4 * kNT;      // scores per chunk: one float4 per thread
-constexpr int kCW = kChunk / 32;     // bitmap words per chunk
+constexpr int kChunk = kTkChunk;     // scores per chunk: one float4 per thread
+static_assert(kChunk == 4 * kNT, "a select workgroup reads one float4 per thread");
+constexpr int kCW = kTkCW;           // bitmap words per chunk
 constexpr int kMaxLen = 64 * kChunk; // longest row
-constexpr int kCap = 512;            // candidate slots per chunk
-constexpr int kLoadC = 4;            // candidate entries per finalize thread (first trip)
+constexpr int kCap = kTkCap;         // candidate slots per chunk
+constexpr int kLoadC = kTkLoad / kNT; // candidate entries per finalize thread (first trip)
 constexpr int kRNT = 512;            // threads of a row workgroup (many-row batches)
 constexpr int kRNW = kRNT / 64;      // its waves
 constexpr int kRJ = 32;              // float4 slots per thread per segment
@@ -248,12 +251,15 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   if (tid < 4) red[tid] = 0u;
   __syncthreads();
   if (tid < nch && (my_cnt >> 16) > (1u << sl)) flag = 1u;
+  // candidate validity without branches: every count read first (chunk f >> sl <= 63, as
+  // 2^sl >= 64 for rows of at most 64 chunks; chunks past the row read 0)
+  uint32_t cn[kLoadC];
+#pragma unroll
+  for (int u = 0; u < kLoadC; ++u) cn[u] = scnt[(tid + u * kNT) >> sl];
   uint32_t cvalid = 0;
 #pragma unroll
-  for (int u = 0; u < kLoadC; ++u) {
-    const int f = tid + u * kNT, sc = f >> sl;
-    cvalid |= (uint32_t)(sc < nch && (uint32_t)(f & ((1 << sl) - 1)) < (scnt[sc] >> 16)) << u;
-  }
+  for (int u = 0; u < kLoadC; ++u)
+    cvalid |= (uint32_t)((uint32_t)((tid + u * kNT) & ((1 << sl) - 1)) < (cn[u] >> 16)) << u;
   __syncthreads();                                        // flag
   const bool streamed = flag != 0u;
   const uint32_t need = (uint32_t)k - G;                  // 1 <= need <= #candidates
@@ -741,7 +747,8 @@ dsa_status dsa_indexer_scores_hist(const dsa_batch* batch, int32_t H, int32_t D,
                                    dsa_dtype scale_dtype, const void* q_codes, const void* q_scale,
                                    const void* w, const void* k_cache, const void* k_scale,
                                    float* scores, int64_t ld, uint32_t* hist, int32_t k,
-                                   void* stream, const char* fn, const dsa_paging* paging);
+                                   void* stream, const char* fn, const dsa_paging* paging,
+                                   bool validate_only = false);
 
 static dsa_status indexer_topk(const dsa_batch* bt, const dsa_paging* pg, int32_t H, int32_t D,
                                dsa_dtype code_dtype, dsa_dtype scale_dtype, const void* q_codes,
@@ -782,7 +789,8 @@ dsa_status dsa_indexer_prolog_scores_hist(const dsa_prolog_cfg* cfg, const dsa_b
                                           const void* q_in, const float* q_cos, const float* q_sin,
                                           const void* k_in, const void* w, void* q_codes, void* q_scale,
                                           void* k_cache, void* k_scale, float* scores, int64_t ld,
-                                          uint32_t* hist, int32_t k, void* stream, const char* fn);
+                                          uint32_t* hist, int32_t k, void* stream, const char* fn,
+                                          bool validate_only = false);
 
 // dsa_indexer_prolog followed by dsa_indexer_topk; where the shapes suit it the prolog runs inside
 // the indexer kernel (each indexer workgroup quantizes its sequence's query rows itself and the
@@ -820,4 +828,112 @@ extern "C" dsa_status dsa_indexer_topk_paged(const dsa_batch* bt, const dsa_pagi
   if (!paging) return fail(DSA_ERR_INVALID_ARG, "%s: paging is NULL", fn);
   return indexer_topk(bt, paging, H, D, code_dtype, scale_dtype, q_codes, q_scale, w, k_cache,
                       k_scale, scores, ld, k, idx, ws, ws_bytes, stream, fn);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Deepseek Indexer Attention in one call.
+dsa_status dsa_sfa_internal(const dsa_batch* bt, int32_t Hq, const void* q, const void* kv,
+                            int64_t kv_row_stride, const int32_t* idx, int32_t k, const float* sink,
+                            float scale, void* out, void* ws, size_t ws_bytes,
+                            const dsa_host::SfaSel* sel, void* stream, const char* fn,
+                            bool validate_only);
+
+// An upper bound of dsa_sparse_attn_workspace_size(t, Hq, k) over every t <= T that grows with
+// T (the attention's partials are not monotone in t): t * n_split * Hq rows of 512 bf16 values
+// plus (max, sum), with t * n_split < 256 / n_hg + t, and no partials once t * n_hg >= 256.
+static size_t sfa_ws_bound(int32_t T, int32_t Hq) {
+  const long n_hg = (Hq + 31) / 32;
+  const long rows = std::min(256 / n_hg + (long)T, 512 / n_hg) * (long)Hq;
+  return align256((size_t)rows * 512 * 2) + align256((size_t)rows * 2 * 4);
+}
+
+extern "C" size_t dsa_indexer_attention_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k,
+                                                       int32_t Hq) {
+  if (num_q <= 0 || max_kv_len <= 0 || Hq <= 0) return 0;
+  return dsa_topk_workspace_size(num_q, max_kv_len, k) + sfa_ws_bound(num_q, Hq);
+}
+
+// Workspace: the top-k's row histograms at the start (zero between calls); the top-k's other
+// regions against the end of the buffer, the attention's split partials just before them.  A
+// buffer sized for the largest num_q and max_kv_len keeps every call's end-packed regions past
+// every call's histograms (the partials' bound grows with num_q).
+extern "C" dsa_status dsa_indexer_attention(const dsa_batch* bt, const dsa_dia* d, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  const char* fn = "dsa_indexer_attention";
+  if (!bt || !d) return fail(DSA_ERR_INVALID_ARG, "%s: batch/args is NULL", fn);
+  dsa_status st = dsa_check_batch(bt, fn);
+  if (st != DSA_OK) return st;
+  if (d->prolog) {
+    st = dsa_check_prolog_cfg(d->prolog, fn);
+    if (st != DSA_OK) return st;
+    const dsa_prolog_cfg* c = d->prolog;
+    if (c->H != d->H || c->D != d->D || c->code_dtype != d->code_dtype || c->scale_dtype != d->scale_dtype)
+      return fail(DSA_ERR_INVALID_ARG, "%s: H, D, code_dtype and scale_dtype must equal the prolog's", fn);
+  }
+  if (bt->num_q == 0) return DSA_OK;
+  const size_t need = dsa_indexer_attention_workspace_size(bt->num_q, bt->max_kv_len, d->k, d->Hq);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  dsa::TkArgs a{};
+  st = topk_prepare(bt, d->scores, d->ld, d->k, d->idx, ws, ws_bytes, fn, &a);
+  if (st != DSA_OK) return st;
+  // the attention's partials end where the top-k's end-packed regions begin (at or past
+  // ws + histograms + sfa_ws_bound, by the size check above)
+  const size_t sfa_bytes = align256(dsa_sparse_attn_workspace_size(bt->num_q, d->Hq, d->k));
+  char* sfa_ws = (char*)a.bg - sfa_bytes;
+  const bool rows = bt->num_q >= dsa::kRowMinT;          // one workgroup per row: own histogram
+  const bool fused_hist = !rows && bt->max_q_per_seq <= 4;
+  // The attention resolves its own slices where that measured faster than the finalize launch
+  // it replaces: at most 16 query tokens on rows of at most 65536 positions (every attention
+  // workgroup of a token repeats the row's k-th key search, whose cost grows with the row,
+  // while the finalize spreads it over the row's chunks).  DSA_DIA_SCHEDULE=slice|finalize
+  // forces one form (testing).
+  bool slice = !rows && bt->num_q <= 16 && bt->max_kv_len <= 65536;
+  if (const char* e = getenv("DSA_DIA_SCHEDULE")) {
+    if (!strcmp(e, "slice")) slice = !rows;
+    else if (!strcmp(e, "finalize")) slice = false;
+  }
+  dsa_host::SfaSel sel{d->scores, d->ld, a.bg, a.cnt, a.bits, a.slots, a.hist, a.nch, d->idx};
+  // every argument first
+  uint32_t* hist = fused_hist ? a.hist : nullptr;
+  if (d->prolog)
+    st = dsa_indexer_prolog_scores_hist(d->prolog, bt, d->q_in, d->q_cos, d->q_sin, d->k_in, d->w,
+                                        d->q_codes, d->q_scale, d->k_cache, d->k_scale, d->scores,
+                                        d->ld, hist, d->k, stream, fn, /*validate_only=*/true);
+  else
+    st = dsa_indexer_scores_hist(bt, d->H, d->D, d->code_dtype, d->scale_dtype, d->q_codes,
+                                 d->q_scale, d->w, d->k_cache, d->k_scale, d->scores, d->ld, hist,
+                                 d->k, stream, fn, nullptr, /*validate_only=*/true);
+  if (st != DSA_OK) return st;
+  st = dsa_sfa_internal(bt, d->Hq, d->q, d->kv, d->kv_row_stride, d->idx, d->k, d->sink, d->scale,
+                        d->out, sfa_ws, sfa_bytes, slice ? &sel : nullptr, stream, fn, true);
+  if (st != DSA_OK) return st;
+  // then the launches: indexer (+ prolog, + first-digit histogram), the top-k's select pass,
+  // the attention resolving its own slices, the merge; or the finalize pass before the
+  // attention; or, for many-row batches, the indexer, the row top-k and the attention
+  if (d->prolog)
+    st = dsa_indexer_prolog_scores_hist(d->prolog, bt, d->q_in, d->q_cos, d->q_sin, d->k_in, d->w,
+                                        d->q_codes, d->q_scale, d->k_cache, d->k_scale, d->scores,
+                                        d->ld, hist, d->k, stream, fn);
+  else
+    st = dsa_indexer_scores_hist(bt, d->H, d->D, d->code_dtype, d->scale_dtype, d->q_codes,
+                                 d->q_scale, d->w, d->k_cache, d->k_scale, d->scores, d->ld, hist,
+                                 d->k, stream, fn, nullptr);
+  if (st != DSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows) {
+    hipLaunchKernelGGL(dsa::topk_row, dim3((unsigned)a.T), dim3(dsa::kRNT), 0, s, a);
+  } else {
+    if (!fused_hist)
+      hipLaunchKernelGGL(dsa::topk_hist, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
+    if (a.poison)                                        // written by select before it is read
+      dsa_host::poison_fill(a.bg, (size_t)((const char*)(a.slots + (size_t)a.T * a.nch * dsa::kCap) - (const char*)a.bg), s);
+    hipLaunchKernelGGL(dsa::topk_select, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
+    if (!slice)
+      hipLaunchKernelGGL(dsa::topk_finalize, dim3((unsigned)a.nch, (unsigned)a.T), dim3(dsa::kNT), 0, s, a);
+  }
+  st = dsa_sfa_internal(bt, d->Hq, d->q, d->kv, d->kv_row_stride, d->idx, d->k, d->sink, d->scale,
+                        d->out, sfa_ws, sfa_bytes, slice ? &sel : nullptr, stream, fn, false);
+  if (st != DSA_OK) return st;
+  return dsa_host::check_launch(fn);
 }

@@ -14,8 +14,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (DSA_BF16, DSA_F16, DSA_F32, DSA_FP8_E4M3, DSA_I8, DsaBatch, DsaPaging, DsaPrologCfg,
-                   DsaProjections, check, lib)
+from ._lib import (DSA_BF16, DSA_F16, DSA_F32, DSA_FP8_E4M3, DSA_I8, DsaBatch, DsaDia, DsaPaging,
+                   DsaPrologCfg, DsaProjections, check, lib)
 
 D_QK, D_V = 576, 512
 
@@ -380,6 +380,57 @@ def dsa_sparse_attn_merge(batch: Batch, Hq: int, k: int, sink: Optional[torch.Te
         ctypes.byref(b), Hq, k, _ptr(sink), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream()))
     return out
+
+
+def dsa_indexer_attention_workspace_size(num_q: int, max_kv_len: int, k: int, Hq: int) -> int:
+    return int(lib.dsa_indexer_attention_workspace_size(num_q, max_kv_len, k, Hq))
+
+
+def dsa_indexer_attention(batch: Batch, H: int, D: int, code: str, scale_dt: str, *, q_codes,
+                          q_scale, w, k_cache, k_scale, k: int, q: torch.Tensor, kv: torch.Tensor,
+                          sink: Optional[torch.Tensor], scale: float, q_in=None, k_in=None,
+                          q_cos=None, q_sin=None, rope_dim=0, rope_offset=0,
+                          rope_interleaved=False, hadamard=False, round_scale=False,
+                          scores: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Indexer (with the prolog when q_in is given), top-k and sparse attention of a decode step
+    in one call -> (idx int32 [T, k], out bf16 [T, Hq, 512]).  With q_in, q_codes/q_scale
+    receive the quantized query and token t's new key row (k_in row t) is written at cache row
+    kv_start[q_seq[t]] + q_pos[t]; `scores` is written as by dsa_indexer_scores."""
+    if code not in _CODE or scale_dt not in _SCALE:
+        raise ValueError("code must be 'i8'|'e4m3', scale_dt 'f16'|'f32'")
+    T = batch.num_q
+    scores = _indexer_operands(batch, H, D, code, scale_dt, q_codes, q_scale, w, k_cache, k_scale,
+                               scores)
+    cfg = None
+    if q_in is not None:
+        in_dt = q_in.dtype
+        if in_dt not in (torch.bfloat16, torch.float32):
+            raise ValueError("inputs must be bf16 or fp32")
+        _need(q_in, "q_in", in_dt, (T, H, D))
+        _need(k_in, "k_in", in_dt, (T, D))
+        if rope_dim:
+            _need(q_cos, "q_cos", torch.float32, (T, rope_dim // 2))
+            _need(q_sin, "q_sin", torch.float32, (T, rope_dim // 2))
+        cfg = DsaPrologCfg(H, D, rope_dim, rope_offset, int(rope_interleaved), int(hadamard),
+                           int(round_scale), DSA_BF16 if in_dt == torch.bfloat16 else DSA_F32,
+                           _CODE[code], _SCALE[scale_dt])
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_codes.device)
+    _need(idx, "idx", torch.int32, (T, k))
+    Hq, _, out, _ = _sfa_args(batch, q, kv, idx, sink, out, None, want_ws=False)
+    if ws is None:
+        ws = _workspace(dsa_indexer_attention_workspace_size(T, batch.max_kv_len, k, Hq), q.device)
+    _need(ws, "ws", torch.uint8)
+    d = DsaDia(ctypes.pointer(cfg) if cfg is not None else None, _ptr(q_in), _ptr(q_cos),
+               _ptr(q_sin), _ptr(k_in), H, D, _CODE[code], _SCALE[scale_dt], _ptr(q_codes),
+               _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(scores),
+               scores.shape[1] if scores.dim() == 2 else 0, k, _ptr(idx), Hq, _ptr(q), _ptr(kv),
+               kv.stride(0), _ptr(sink), ctypes.c_float(scale), _ptr(out))
+    b = batch.c()
+    check("dsa_indexer_attention", lib.dsa_indexer_attention(
+        ctypes.byref(b), ctypes.byref(d), _ptr(ws), ws.numel(), _stream()))
+    return idx, out
 
 
 def _indexer_operands(batch, H, D, code, scale_dt, q_codes, q_scale, w, k_cache, k_scale, scores):

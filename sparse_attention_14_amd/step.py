@@ -1,5 +1,6 @@
-"""One DSA decode step through the C ABI: prolog -> indexer scores + top-k -> sparse attention
-(the prolog inside the indexer kernel where the library supports that form).
+"""One DSA decode step through the C ABI: prolog -> indexer scores + top-k -> sparse attention,
+in one call (dsa_indexer_attention: the prolog inside the indexer kernel where the library
+supports that form, the attention resolving its own slices of the selection) or as separate calls.
 
 [DIA] "Deepseek Indexer Attention" (jsqmd.com/news/787325): the decode layer runs the indexer
 prolog, the Lightning Indexer with its TopK and Sparse Flash Attention in that order (the MLA
@@ -14,9 +15,9 @@ from typing import Optional
 import torch
 
 from ._lib import DSA_ERR_UNSUPPORTED, DsaError
-from .dsa import (Batch, _scores_ld, dsa_indexer_prolog, dsa_indexer_prolog_topk,
-                  dsa_indexer_topk, dsa_sparse_attn_decode, dsa_sparse_attn_workspace_size,
-                  dsa_topk_workspace_size)
+from .dsa import (Batch, _scores_ld, dsa_indexer_attention, dsa_indexer_attention_workspace_size,
+                  dsa_indexer_prolog, dsa_indexer_topk, dsa_sparse_attn_decode,
+                  dsa_sparse_attn_workspace_size, dsa_topk_workspace_size)
 
 
 @dataclass
@@ -41,6 +42,7 @@ class StepBuffers:
     out: torch.Tensor
     ws_topk: torch.Tensor
     ws_sfa: Optional[torch.Tensor]
+    ws_dia: torch.Tensor            # the one-call path's workspace (zero-filled once)
 
     @staticmethod
     def alloc(batch: Batch, cfg: IndexerCfg, Hq: int, device="cuda") -> "StepBuffers":
@@ -56,7 +58,9 @@ class StepBuffers:
             out=torch.empty((T, Hq, 512), dtype=torch.bfloat16, device=device),
             ws_topk=torch.zeros(max(1, dsa_topk_workspace_size(T, batch.max_kv_len, cfg.k)),
                                 dtype=torch.uint8, device=device),
-            ws_sfa=torch.empty(nws, dtype=torch.uint8, device=device) if nws else None)
+            ws_sfa=torch.empty(nws, dtype=torch.uint8, device=device) if nws else None,
+            ws_dia=torch.zeros(max(1, dsa_indexer_attention_workspace_size(T, batch.max_kv_len, cfg.k, Hq)),
+                               dtype=torch.uint8, device=device))
 
 
 def decode_step(batch: Batch, cfg: IndexerCfg, *, q_in, k_in, new_slots, w, k_cache, k_scale,
@@ -68,30 +72,30 @@ def decode_step(batch: Batch, cfg: IndexerCfg, *, q_in, k_in, new_slots, w, k_ca
     (bf16 or fp32); new_slots [T] int64: cache rows of the new tokens' keys (row
     kv_start[q_seq[t]] + q_pos[t] of the batch layout); k_cache/k_scale: the quantized indexer
     key cache; q_attn [T, Hq, 576] bf16, kv [N, 576] bf16, sink [Hq].
-    With `fused` the prolog runs inside the indexer kernel (dsa_indexer_prolog_topk; the keys'
-    rotary tables are the tokens' own, q_cos/q_sin) wherever the library supports that form, and
-    as its own launch otherwise.  Returns buf.out [T, Hq, 512] bf16.
+    With `fused` the whole step is one call (dsa_indexer_attention; the keys' rotary tables are
+    the tokens' own, q_cos/q_sin), else the separate calls dsa_indexer_prolog,
+    dsa_indexer_topk and dsa_sparse_attn_decode.  Returns buf.out [T, Hq, 512] bf16 (buf.idx
+    holds the selection, buf.scores the indexer scores).
     """
-    done = False
     if fused:
         try:
-            dsa_indexer_prolog_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, k_in=k_in,
-                                    w=w, q_codes=buf.q_codes, q_scale=buf.q_scale, k_cache=k_cache,
-                                    k_scale=k_scale, k=cfg.k, q_cos=q_cos, q_sin=q_sin,
-                                    rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
-                                    rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard,
-                                    scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
-            done = True
+            dsa_indexer_attention(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_codes=buf.q_codes,
+                                  q_scale=buf.q_scale, w=w, k_cache=k_cache, k_scale=k_scale,
+                                  k=cfg.k, q=q_attn, kv=kv, sink=sink, scale=scale, q_in=q_in,
+                                  k_in=k_in, q_cos=q_cos, q_sin=q_sin, rope_dim=cfg.rope_dim,
+                                  rope_offset=cfg.rope_offset,
+                                  rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard,
+                                  scores=buf.scores, idx=buf.idx, out=buf.out, ws=buf.ws_dia)
+            return buf.out
         except DsaError as e:
             if e.status != DSA_ERR_UNSUPPORTED:
                 raise
-    if not done:
-        dsa_indexer_prolog(cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, q_cos=q_cos,
-                           q_sin=q_sin, q_codes=buf.q_codes, q_scale=buf.q_scale, k_in=k_in,
-                           k_cos=k_cos, k_sin=k_sin, k_slot=new_slots, k_cache=k_cache,
-                           k_scale=k_scale, rope_dim=cfg.rope_dim, rope_offset=cfg.rope_offset,
-                           rope_interleaved=cfg.rope_interleaved, hadamard=cfg.hadamard)
-        dsa_indexer_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
-                         k_cache, k_scale, cfg.k, scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
+    dsa_indexer_prolog(cfg.H, cfg.D, cfg.code, cfg.scale_dt, q_in=q_in, q_cos=q_cos, q_sin=q_sin,
+                       q_codes=buf.q_codes, q_scale=buf.q_scale, k_in=k_in, k_cos=k_cos, k_sin=k_sin,
+                       k_slot=new_slots, k_cache=k_cache, k_scale=k_scale, rope_dim=cfg.rope_dim,
+                       rope_offset=cfg.rope_offset, rope_interleaved=cfg.rope_interleaved,
+                       hadamard=cfg.hadamard)
+    dsa_indexer_topk(batch, cfg.H, cfg.D, cfg.code, cfg.scale_dt, buf.q_codes, buf.q_scale, w,
+                     k_cache, k_scale, cfg.k, scores=buf.scores, idx=buf.idx, ws=buf.ws_topk)
     return dsa_sparse_attn_decode(batch, q_attn, kv, buf.idx, sink, scale, out=buf.out,
                                   ws=buf.ws_sfa)

@@ -204,3 +204,52 @@ def test_projections_validation_before_any_device_call():
     assert lib.dsa_indexer_projections(ctypes.byref(args(T=0)), None, 0, None) == L.DSA_OK
     assert lib.dsa_indexer_projections_workspace_size(8, 64, 128) >= 8 * 8 * 192 * 4
     assert lib.dsa_indexer_projections_workspace_size(0, 64, 128) == 0
+
+
+def _dia(L, **kw):
+    P = ctypes.c_void_p(0x1000)
+    f = dict(prolog=None, q_in=None, q_cos=None, q_sin=None, k_in=None, H=64, D=128,
+             code_dtype=L.DSA_I8, scale_dtype=L.DSA_F16, q_codes=P, q_scale=P, w=P, k_cache=P,
+             k_scale=P, scores=P, ld=65536, k=2048, idx=P, Hq=128, q=P, kv=P, kv_row_stride=576,
+             sink=P, scale=0.04, out=P)
+    f.update(kw)
+    return L.DsaDia(**f)
+
+
+def test_indexer_attention_validation_before_any_device_call():
+    L = _lib()
+    lib = L.lib
+    b = _batch()
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.dsa_indexer_attention_workspace_size(8, 65536, 2048, 128)
+    # the workspace holds the top-k's part and at least the attention's partials
+    assert need >= lib.dsa_topk_workspace_size(8, 65536, 2048) + lib.dsa_sparse_attn_workspace_size(8, 128, 2048)
+    # its bound on the partials grows with the batch (a buffer sized for the largest batch serves
+    # every smaller one), though the attention's own partials do not
+    for T in range(1, 64):
+        assert lib.dsa_indexer_attention_workspace_size(T + 1, 65536, 2048, 128) >= \
+            lib.dsa_indexer_attention_workspace_size(T, 65536, 2048, 128)
+        assert lib.dsa_indexer_attention_workspace_size(T, 65536, 2048, 128) >= \
+            lib.dsa_topk_workspace_size(T, 65536, 2048) + lib.dsa_sparse_attn_workspace_size(T, 128, 2048)
+    call = lambda d, nbytes=need, w=ws, batch=b: lib.dsa_indexer_attention(ctypes.byref(batch), ctypes.byref(d), w, nbytes, None)
+    assert lib.dsa_indexer_attention(ctypes.byref(b), None, ws, need, None) == L.DSA_ERR_INVALID_ARG
+    assert call(_dia(L), need - 256) == L.DSA_ERR_WORKSPACE
+    assert call(_dia(L), need, None) == L.DSA_ERR_WORKSPACE
+    assert call(_dia(L), need, ctypes.c_void_p(0x100080)) == L.DSA_ERR_INVALID_ARG      # misaligned
+    assert call(_dia(L, k=0)) == L.DSA_ERR_UNSUPPORTED                                      # top-k
+    assert call(_dia(L, H=32)) == L.DSA_ERR_UNSUPPORTED                                     # indexer
+    assert call(_dia(L, q_codes=None)) == L.DSA_ERR_INVALID_ARG
+    assert call(_dia(L, Hq=64)) == L.DSA_ERR_UNSUPPORTED                                    # attention
+    assert call(_dia(L, out=None)) == L.DSA_ERR_INVALID_ARG
+    assert call(_dia(L, kv=ctypes.c_void_p(0x1008))) == L.DSA_ERR_INVALID_ARG
+    # with a prolog: its dims and dtypes must match the indexer's
+    cfg = L.DsaPrologCfg(64, 128, 64, 64, 0, 1, 0, L.DSA_BF16, L.DSA_I8, L.DSA_F16)
+    assert call(_dia(L, prolog=ctypes.pointer(cfg), q_in=ctypes.c_void_p(0x1000), k_in=ctypes.c_void_p(0x1000),
+                     q_cos=ctypes.c_void_p(0x1000), q_sin=ctypes.c_void_p(0x1000), scale_dtype=L.DSA_F32)) == L.DSA_ERR_INVALID_ARG
+    assert b"must equal the prolog" in lib.dsa_last_error()
+    assert call(_dia(L, prolog=ctypes.pointer(cfg), q_in=None, k_in=ctypes.c_void_p(0x1000),
+                     q_cos=ctypes.c_void_p(0x1000), q_sin=ctypes.c_void_p(0x1000))) == L.DSA_ERR_INVALID_ARG
+    # an empty batch is a no-op that needs no workspace
+    e = _batch(T=0, B=0, mq=0, ml=0)
+    assert call(_dia(L), 0, None, e) == L.DSA_OK
+    assert lib.dsa_indexer_attention_workspace_size(0, 65536, 2048, 128) == 0

@@ -2,9 +2,9 @@
 bytes before use and the library fill its written-before-read workspace regions the same way
 (NaN as fp32/bf16, -1 as int, every bit set in a bitmap).  A read of LDS or workspace data before
 the kernel's own write then changes the results.  Each case runs the indexer + top-k (fused and
-separate), the attention and the fused prolog entry three times -- normal, poisoned, normal -- and
-requires bit-identical outputs (determinism and no read-before-write).  Selections are range-checked
-on the host before the attention consumes them.
+separate), the attention, the fused prolog entry and the one-call path (both schedules) three
+times -- normal, poisoned, normal -- and requires bit-identical outputs (determinism and no
+read-before-write).  Selections are range-checked on the host before the attention consumes them.
 """
 import os
 
@@ -66,8 +66,22 @@ def run_once(wl):
             os.environ.pop("DSA_PROLOG_SCHEDULE", None)
         torch.cuda.synchronize()
         fused.append((qc, qs, idx3))
+    # the one-call path in both schedules
+    dia = []
+    for sched in ("slice", "finalize"):
+        os.environ["DSA_DIA_SCHEDULE"] = sched
+        try:
+            i4, o4 = dsa.dsa_indexer_attention(
+                g.batch, c.H, c.D, c.code, c.scale_dt, q_codes=g.q_codes, q_scale=g.q_scale, w=d["w"],
+                k_cache=g.k_cache, k_scale=g.k_scale, k=k, q=d["q"], kv=d["kv"],
+                sink=d["sink"] if g.wl.spec.sink else None, scale=g.wl.scale)
+        finally:
+            os.environ.pop("DSA_DIA_SCHEDULE", None)
+        torch.cuda.synchronize()
+        valid_idx(i4, wl.q_pos, k)
+        dia += [i4, o4]
     vis = torch.arange(sc.shape[1], device="cuda")[None, :] <= g.d["q_pos"][:, None].long()
-    return {"q_codes": g.q_codes, "q_scale": g.q_scale, "scores": sc[vis], "idx": idx, "out": out,
+    return {**{f"dia_{i}": v for i, v in enumerate(dia)},"q_codes": g.q_codes, "q_scale": g.q_scale, "scores": sc[vis], "idx": idx, "out": out,
             "scores_sep": sc2[vis], "idx_sep": idx2,
             **{f"{n}_{i}": v for i, f in enumerate(fused) for n, v in zip(("qc", "qs", "idx_fused"), f)}}
 
@@ -92,4 +106,6 @@ def test_poisoned_runs_are_bit_identical(case):
     again = run_once(wl)
     same(ref, again, "second normal run")
     same(ref, pois, "poisoned run")
+    assert torch.equal(ref["dia_0"], ref["idx"]) and torch.equal(ref["dia_2"], ref["idx"])
+    assert torch.equal(ref["dia_1"], ref["out"]) and torch.equal(ref["dia_3"], ref["out"])
     log(f"  {len(ref)} outputs bit-identical across normal, poisoned, normal")
