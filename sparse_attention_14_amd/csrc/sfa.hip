@@ -704,8 +704,10 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
 
 // Merge split partials: with a_s = O_s / l_s (stored bf16), m_s, l_s (fp32) per split,
 //   o = sum_s 2^(m_s - M) l_s a_s / (sum_s 2^(m_s - M) l_s + 2^(sink - M)),  M = max(m_s, sink).
-// One wave per (token, head): lane s reads split s's (m, l) (n_split <= 64), the wave reduces
-// them with shuffles, then each lane accumulates 8 value dims over the splits.  Workgroups are
+// One wave per (token, head), lane = 8 value dims.  One memory round trip: the first kPre
+// splits' partial outputs (addresses clamped to the last split, weighted 0 past it) and every
+// split's (m, l), lane s holding split s (n_split <= 64); the maxima and weights then move across
+// lanes with v_readlane (uniform loops over the splits, no LDS round trips).  Workgroups are
 // ordered like the split kernel's (xcd_remap over token-major ids), so a token's partials are
 // read on the XCD whose L2 received them.
 __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
@@ -713,32 +715,21 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   const int lane = threadIdx.x & 63;
   const int th = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
-  const int t = th / a.Hq, h = th % a.Hq;
-  const u16* src = a.ws_o + (((long)t * a.n_split) * a.Hq + h) * kDv + lane * 8;
+  const int t = th / a.Hq, h = th % a.Hq, ns = a.n_split;
+  const u16* src = a.ws_o + (((long)t * ns) * a.Hq + h) * kDv + lane * 8;
   const long sstride = (long)a.Hq * kDv;
-  // one memory round trip: the first kPre splits' partial outputs and every split's (m, l)
   uint4 pv[kPre];
 #pragma unroll
-  for (int sp = 0; sp < kPre; ++sp) {
-    pv[sp] = uint4{0u, 0u, 0u, 0u};
-    if (sp < a.n_split) pv[sp] = *reinterpret_cast<const uint4*>(src + sp * sstride);
-  }
+  for (int sp = 0; sp < kPre; ++sp) pv[sp] = *reinterpret_cast<const uint4*>(src + min(sp, ns - 1) * sstride);
+  const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (((long)t * ns + min(lane, ns - 1)) * a.Hq + h) * 2);
   const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-  float ms = -INFINITY, ls = 0.f;
-  if (lane < a.n_split) {
-    const long base = ((long)t * a.n_split + lane) * a.Hq + h;
-    ms = a.ws_ml[base * 2];
-    ls = a.ws_ml[base * 2 + 1];
-  }
-  float M = ms;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-  M = fmaxf(M, sk);
-  const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M) * ls;   // split weight
-  float den = f;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
-  den += (sk == -INFINITY) ? 0.f : exp2f(sk - M);
+  auto lane_f = [](float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+  };
+  float M = sk;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, lane_f(ml.x, sp));
+  const float f = (lane < ns && ml.x != -INFINITY) ? exp2f(ml.x - M) * ml.y : 0.f;   // split weight
+  float den = (sk == -INFINITY) ? 0.f : exp2f(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](float fs, const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -749,9 +740,13 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
     }
   };
 #pragma unroll
-  for (int sp = 0; sp < kPre; ++sp) add(__shfl(f, sp, kWave), pv[sp]);   // 0 past n_split
-  for (int sp = kPre; sp < a.n_split; ++sp)
-    add(__shfl(f, sp, kWave), *reinterpret_cast<const uint4*>(src + sp * sstride));
+  for (int sp = 0; sp < kPre; ++sp)
+    if (sp < ns) { const float fs = lane_f(f, sp); den += fs; add(fs, pv[sp]); }
+  for (int sp = kPre; sp < ns; ++sp) {
+    const float fs = lane_f(f, sp);
+    den += fs;
+    add(fs, *reinterpret_cast<const uint4*>(src + sp * sstride));
+  }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint4 pk;
   pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
