@@ -173,6 +173,6 @@ void poison_fill(void* p, size_t bytes, hipStream_t s);
 struct SfaSel {
   const float* scores; long ld;
   const uint32_t* bg; const uint32_t* cnt; const uint32_t* bits; const uint64_t* slots;
-  uint32_t* hist; int nch; int32_t* idx;
+  uint32_t* hist; uint32_t* hist2; int nch; int32_t* idx;
 };
 }  // namespace dsa_host

@@ -52,13 +52,14 @@ struct SfaArgs {
   int T, B, Hq, n_hg, n_split, kps;
   const int32_t* bt; int bps; int bs_log2;   // paged cache: block table (NULL: flat rows)
   int poison;                                // debug: poison LDS before use
-  // selection resolved by the kernel itself (sfa_kernel<., true>) from the top-k select pass's
-  // state: the rows' scores (overflow rows re-read them), query positions, the per-row
+  // selection resolved by the kernel itself (sfa_kernel<false, true>) from the top-k select
+  // pass's state: the rows' scores (overflow rows re-read them), query positions, the per-row
   // threshold digit and count above it, per-chunk counts, bitmaps and candidate slots, the
-  // digit histograms (zeroed here for the next call) and the index output (may be NULL)
+  // first-digit histograms (zeroed by the attention for the next call), the candidates'
+  // second-digit histograms (zeroed by the merge) and the index output (may be NULL)
   const int32_t* q_pos; const float* scores; long ld;
   const uint32_t* tk_bg; const uint32_t* tk_cnt; const uint32_t* tk_bits; const uint64_t* tk_slots;
-  uint32_t* tk_hist; int tk_nch; int32_t* idx_out;
+  uint32_t* tk_hist; uint32_t* tk_hist2; int tk_nch; int32_t* idx_out;
 };
 constexpr int kMaxBps = 2048;                        // paged: block-table entries per sequence
 
@@ -241,8 +242,11 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
 // slice_loads issues the one memory round trip (before the workgroup's Q loads, so that waiting
 // for it does not wait for them); select_slice then works in LDS only, with LDS-only barriers.
 // `scr` is LDS scratch: 2 x 32 KiB of row bitmaps and 9 KiB of histogram and counters.  Rows
-// whose candidate lists overflow the first trip re-read the row's scores.  The slice ends in
-// sidx, not yet behind a barrier.
+// whose candidate lists overflow the first trip re-read the row's scores.  The select pass also
+// counted the candidates' second digits per row (hist2): the second digit b2 is one scan of
+// those counts, and the k-th key is ranked among the few candidates in bin b2 by one wave
+// (a third histogram pass only when that bin holds more than 64 keys, or on overflow rows).
+// The slice ends in sidx, not yet behind a barrier.
 constexpr int kSelNT = 512;                            // threads of the attention workgroup
 constexpr int kSelLoad = kTkLoad / kSelNT;             // first-trip candidate entries per thread
 constexpr int kSelG = 4;                               // 16-byte bitmap groups per thread (<= 64 chunks)
@@ -251,6 +255,7 @@ struct SliceIn {
   uint32_t b1, G, my_cnt;
   uint64_t ev[kSelLoad];
   uint4 wv[kSelG];
+  uint4 h2;                                            // second-digit bins 2047 - 4 tid - 3 .. 2047 - 4 tid
 };
 
 __device__ __forceinline__ SliceIn slice_loads(const SfaArgs& a, int t) {
@@ -280,6 +285,7 @@ __device__ __forceinline__ SliceIn slice_loads(const SfaArgs& a, int t) {
     const uint32_t m = own ? 0xFFFFFFFFu : 0u;
     in.wv[j] = uint4{v.x & m, v.y & m, v.z & m, v.w & m};
   }
+  in.h2 = reinterpret_cast<const uint4*>(a.tk_hist2 + (long)t * kHistBins)[kHistBins / 4 - 1 - tid];
   return in;
 }
 
@@ -307,12 +313,19 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
   uint4* tie = sel + 64 * kTkCW / 4;                   // [64 * kTkCW / 4] positions with key K*
   uint32_t* h = reinterpret_cast<uint32_t*>(tie + 64 * kTkCW / 4);   // [kHistBins]
   uint32_t* sh = h + kHistBins;                        // [NT / 64]
-  uint32_t* res = sh + NT / 64;                        // [2]
-  uint32_t* flag = res + 2;                            // [1]
-  uint32_t* scnt = flag + 2;                           // [64]
-  for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
-  if (tid < 64) scnt[tid] = tid < nch ? in.my_cnt : 0u;   // tid < nch <= nch_m
-  if (tid == 0) *flag = 0u;
+  uint32_t* res = sh + NT / 64;                        // [4]
+  uint32_t* flag = res + 4;                            // [1]
+  uint32_t* n3 = flag + 1;                             // [1]
+  uint32_t* scnt = n3 + 2;                             // [64]
+  uint32_t* list = scnt + 64;                          // [64] candidates in bin b2
+  uint32_t* kres = list + 64;                          // [4] K*, keys equal to it, ties kept
+  if (tid < 64) {                                      // wave 0
+    scnt[tid] = tid < nch ? in.my_cnt : 0u;            // tid < nch <= nch_m
+    // does any chunk's candidate list overflow the first trip?
+    const bool ov = tid < nch && (in.my_cnt >> 16) > (1u << sl);
+    const bool any_ov = __ballot(ov) != 0;
+    if (tid == 0) { *flag = any_ov; *n3 = 0u; }
+  }
   // selects below are written as masks: a select between two arrays becomes a select of
   // addresses, which puts both in scratch memory
   auto masked = [](uint4 v, bool keep) {
@@ -325,7 +338,6 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
     if (j < gpt && gi < ngr) { sel[gi] = masked(in.wv[j], gi < gvalid); tie[gi] = uint4{0u, 0u, 0u, 0u}; }
   }
   block_barrier<true>();
-  if (tid < nch && (in.my_cnt >> 16) > (1u << sl)) *flag = 1u;
   // candidate validity without branches: every count first (chunk f >> sl <= 63; chunks past
   // the row read 0)
   uint32_t cn[kSelLoad];
@@ -335,7 +347,6 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
 #pragma unroll
   for (int u = 0; u < kSelLoad; ++u)
     cvalid |= (uint32_t)((uint32_t)((tid + u * NT) & ((1 << sl) - 1)) < (cn[u] >> 16)) << u;
-  block_barrier<true>();                               // flag
   const bool streamed = *flag != 0u;
   const uint32_t b1 = in.b1;
   const uint32_t need = (uint32_t)k - in.G;            // 1 <= need <= #candidates
@@ -361,22 +372,61 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
       }
     }
   };
-  each_cand([&](uint32_t key, uint32_t) { atomicAdd(&h[(key >> 10) & 0x7FFu], 1u); });
-  block_barrier<true>();
-  find_digit_desc<NT, true>(h, need, sh, res);
-  const uint32_t b2 = res[0];
-  const uint32_t need2 = need - res[1];                // >= 1, among the b2 bin
-  block_barrier<true>();
-  for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
-  block_barrier<true>();
-  each_cand([&](uint32_t key, uint32_t) {
-    if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h[key & 0x3FFu], 1u);
-  });
-  block_barrier<true>();
-  find_digit_desc<NT, true>(h, need2, sh, res);
-  const uint32_t kstar = (b1 << 21) | (b2 << 10) | res[0];
-  const uint32_t n_eq = h[res[0]];
-  const uint32_t take_eq = need2 - res[1];             // >= 1
+  // ---- the second digit b2 and how many candidates share it (c3)
+  uint32_t b2, need2, c3;
+  if (!streamed) {                                     // from the select pass's counts, in registers
+    const uint32_t loc[4] = {in.h2.w, in.h2.z, in.h2.y, in.h2.x};   // bins 2047 - 4 tid - j
+    uint32_t all;
+    uint32_t before = block_excl_scan<NT, true>(loc[0] + loc[1] + loc[2] + loc[3], sh, all);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (before < need && need <= before + loc[j]) {
+        res[0] = kHistBins - 1 - (4 * tid + j); res[1] = before; res[2] = loc[j];
+      }
+      before += loc[j];
+    }
+    block_barrier<true>();
+    b2 = res[0]; need2 = need - res[1]; c3 = res[2];
+  } else {                                             // a histogram pass over the re-read row
+    for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
+    block_barrier<true>();
+    each_cand([&](uint32_t key, uint32_t) { atomicAdd(&h[(key >> 10) & 0x7FFu], 1u); });
+    block_barrier<true>();
+    find_digit_desc<NT, true>(h, need, sh, res);
+    b2 = res[0]; need2 = need - res[1]; c3 = h[b2];
+  }
+  block_barrier<true>();                               // res and h read
+  // ---- the k-th key K* among the candidates of bin b2 (need2 of them rank at or above it)
+  uint32_t kstar, n_eq, take_eq;
+  if (c3 <= 64) {                                      // the bin's keys listed, ranked by one wave
+    each_cand([&](uint32_t key, uint32_t) {
+      if (((key >> 10) & 0x7FFu) == b2) list[atomicAdd(n3, 1u) & 63u] = key;
+    });
+    block_barrier<true>();
+    if (tid < 64) {
+      const uint32_t key = tid < (int)c3 ? list[tid] : 0u;
+      uint32_t gt = 0, eq = 0;
+      for (uint32_t j = 0; j < c3; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, (int)j);
+        gt += kj > key;
+        eq += kj == key;
+      }
+      if (tid < (int)c3 && gt < need2 && need2 <= gt + eq) { kres[0] = key; kres[1] = eq; kres[2] = need2 - gt; }
+    }
+    block_barrier<true>();
+    kstar = kres[0]; n_eq = kres[1]; take_eq = kres[2];
+  } else {                                             // a third-digit histogram pass
+    for (int i = tid; i < kHistBins; i += NT) h[i] = 0u;
+    block_barrier<true>();
+    each_cand([&](uint32_t key, uint32_t) {
+      if (((key >> 10) & 0x7FFu) == b2) atomicAdd(&h[key & 0x3FFu], 1u);
+    });
+    block_barrier<true>();
+    find_digit_desc<NT, true>(h, need2, sh, res);
+    kstar = (b1 << 21) | (b2 << 10) | res[0];
+    n_eq = h[res[0]];
+    take_eq = need2 - res[1];                          // >= 1
+  }
   uint32_t* selw = reinterpret_cast<uint32_t*>(sel);
   uint32_t* tiew = reinterpret_cast<uint32_t*>(tie);
   each_cand([&](uint32_t key, uint32_t pos) {
@@ -716,6 +766,11 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   const int th = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.T * a.Hq) return;                        // whole waves only; no barriers below
   const int t = th / a.Hq, h = th % a.Hq, ns = a.n_split;
+  if (a.tk_hist2 && h == 0) {                          // read by this call's attention: clear it
+    uint4* h2 = reinterpret_cast<uint4*>(a.tk_hist2 + (long)t * kHistBins);
+#pragma unroll
+    for (int i = 0; i < kHistBins / 4 / 64; ++i) h2[lane + 64 * i] = uint4{0u, 0u, 0u, 0u};
+  }
   const u16* src = a.ws_o + (((long)t * ns) * a.Hq + h) * kDv + lane * 8;
   const long sstride = (long)a.Hq * kDv;
   uint4 pv[kPre];
@@ -842,10 +897,12 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(DSA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (bt->num_q == 0) return DSA_OK;
   if (!q || !kv || !(idx || sel) || !out) return fail(DSA_ERR_INVALID_ARG, "%s: a data pointer is NULL", fn);
-  if (sel && (pg || !sel->scores || sel->nch < 1 || sel->nch > 64))
+  if (sel && (pg || !sel->scores || !sel->hist2 || sel->nch < 1 || sel->nch > 64))
     return fail(DSA_ERR_UNSUPPORTED, "%s: a pending selection needs flat caches and rows of at most 64 chunks", fn);
   if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)out) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q/kv/out must be 16-byte aligned", fn);
   const dsa::SfaPlan p = dsa::plan(bt->num_q, Hq, k);
+  if (sel && p.n_split < 2)                              // the merge clears the second-digit histograms
+    return fail(DSA_ERR_UNSUPPORTED, "%s: a pending selection needs split partials (k > 32)", fn);
   const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
   if (need && (!ws || ws_bytes < need)) return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
   if (need && ((uintptr_t)ws & 255)) return fail(DSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
@@ -863,7 +920,7 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   if (sel) {
     a.idx = nullptr; a.q_pos = bt->q_pos; a.scores = sel->scores; a.ld = sel->ld;
     a.tk_bg = sel->bg; a.tk_cnt = sel->cnt; a.tk_bits = sel->bits; a.tk_slots = sel->slots;
-    a.tk_hist = sel->hist; a.tk_nch = sel->nch; a.idx_out = sel->idx;
+    a.tk_hist = sel->hist; a.tk_hist2 = sel->hist2; a.tk_nch = sel->nch; a.idx_out = sel->idx;
   }
   if (p.n_split > 1) {
     const size_t n = (size_t)bt->num_q * p.n_split * Hq;
@@ -882,14 +939,12 @@ static void sfa_launch_split(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipSt
     dsa_host::poison_fill(a.ws_o, n * dsa::kDv * 2, s);
     dsa_host::poison_fill(a.ws_ml, n * 2 * 4, s);
   }
-  const bool tk = a.tk_bg != nullptr;                    // the kernel resolves its own slice
-  if (p.n_split == 1) {
-    if (tk) hipLaunchKernelGGL((dsa::sfa_kernel<true, true>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((dsa::sfa_kernel<true, false>), grid, dim3(512), 0, s, a);
-  } else {
-    if (tk) hipLaunchKernelGGL((dsa::sfa_kernel<false, true>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((dsa::sfa_kernel<false, false>), grid, dim3(512), 0, s, a);
-  }
+  if (a.tk_bg)                                           // the kernel resolves its own slice
+    hipLaunchKernelGGL((dsa::sfa_kernel<false, true>), grid, dim3(512), 0, s, a);   // n_split > 1
+  else if (p.n_split == 1)
+    hipLaunchKernelGGL((dsa::sfa_kernel<true, false>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((dsa::sfa_kernel<false, false>), grid, dim3(512), 0, s, a);
 }
 
 static void sfa_launch_merge(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipStream_t s) {

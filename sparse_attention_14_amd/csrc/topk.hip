@@ -58,6 +58,7 @@ constexpr int kRowMinT = 256;        // batches of at least this many rows take 
 struct TkArgs {
   const int32_t* q_pos; const float* scores; long ld; int k; int T; int nch;
   int32_t* idx; uint32_t* hist; uint32_t* bg; uint32_t* cnt; uint32_t* bits; uint64_t* slots;
+  uint32_t* hist2;                   // optional [T][kBins]: the candidates' second digits (select)
   int poison;                        // debug: poison LDS before use
 };
 
@@ -160,6 +161,12 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
     eqm |= (uint32_t)(ok && d == b1) << q;
   }
   if (gtm) atomicOr(&bw[tid >> 3], gtm << (4 * (tid & 7)));
+  if (a.hist2 && eqm) {                                  // the row's second-digit histogram
+    uint32_t* h2 = a.hist2 + (long)t * kBins;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if ((eqm >> q) & 1u) atomicAdd(&h2[(keys[q] >> 10) & 0x7FFu], 1u);
+  }
   const uint32_t mine = (uint32_t)__popc(gtm) | ((uint32_t)__popc(eqm) << 16);
   uint32_t tot;
   const uint32_t before = block_excl_scan<kNT>(mine, sh, tot);   // also publishes bw
@@ -847,16 +854,21 @@ static size_t sfa_ws_bound(int32_t T, int32_t Hq) {
   return align256((size_t)rows * 512 * 2) + align256((size_t)rows * 2 * 4);
 }
 
+// The second-digit histograms of the slice schedule (zero at rest, after the first-digit ones).
+static size_t hist2_bytes(int32_t T) { return align256((size_t)T * dsa::kBins * 4); }
+
 extern "C" size_t dsa_indexer_attention_workspace_size(int32_t num_q, int32_t max_kv_len, int32_t k,
                                                        int32_t Hq) {
   if (num_q <= 0 || max_kv_len <= 0 || Hq <= 0) return 0;
-  return dsa_topk_workspace_size(num_q, max_kv_len, k) + sfa_ws_bound(num_q, Hq);
+  return dsa_topk_workspace_size(num_q, max_kv_len, k) + hist2_bytes(num_q) + sfa_ws_bound(num_q, Hq);
 }
 
-// Workspace: the top-k's row histograms at the start (zero between calls); the top-k's other
-// regions against the end of the buffer, the attention's split partials just before them.  A
-// buffer sized for the largest num_q and max_kv_len keeps every call's end-packed regions past
-// every call's histograms (the partials' bound grows with num_q).
+// Workspace: the top-k's row histograms at the start, then the second-digit histograms of the
+// slice schedule (both zero between calls; a later call's first-digit rows may cover an earlier
+// call's second-digit rows, zero as well); the top-k's other regions against the end of the
+// buffer, the attention's split partials just before them.  A buffer sized for the largest
+// num_q and max_kv_len keeps every call's end-packed regions past every call's histograms (the
+// partials' bound grows with num_q).
 extern "C" dsa_status dsa_indexer_attention(const dsa_batch* bt, const dsa_dia* d, void* ws,
                                             size_t ws_bytes, void* stream) {
   const char* fn = "dsa_indexer_attention";
@@ -888,12 +900,17 @@ extern "C" dsa_status dsa_indexer_attention(const dsa_batch* bt, const dsa_dia* 
   // workgroup of a token repeats the row's k-th key search, whose cost grows with the row,
   // while the finalize spreads it over the row's chunks).  DSA_DIA_SCHEDULE=slice|finalize
   // forces one form (testing).
-  bool slice = !rows && bt->num_q <= 16 && bt->max_kv_len <= 65536;
+  // (The merge pass clears the second-digit histograms for the next call: the slice schedule
+  // needs split partials, i.e. k > 32.)
+  const bool splits = dsa_sparse_attn_workspace_size(bt->num_q, d->Hq, d->k) > 0;
+  bool slice = !rows && splits && bt->num_q <= 16 && bt->max_kv_len <= 65536;
   if (const char* e = getenv("DSA_DIA_SCHEDULE")) {
-    if (!strcmp(e, "slice")) slice = !rows;
+    if (!strcmp(e, "slice")) slice = !rows && splits;
     else if (!strcmp(e, "finalize")) slice = false;
   }
-  dsa_host::SfaSel sel{d->scores, d->ld, a.bg, a.cnt, a.bits, a.slots, a.hist, a.nch, d->idx};
+  uint32_t* hist2 = (uint32_t*)((char*)ws + align256((size_t)bt->num_q * dsa::kShards * dsa::kBins * 4));
+  if (slice) a.hist2 = hist2;
+  dsa_host::SfaSel sel{d->scores, d->ld, a.bg, a.cnt, a.bits, a.slots, a.hist, hist2, a.nch, d->idx};
   // every argument first
   uint32_t* hist = fused_hist ? a.hist : nullptr;
   if (d->prolog)

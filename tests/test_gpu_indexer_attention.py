@@ -155,3 +155,7 @@ def test_workspace_shared_across_shapes():
         compare(g, False, ws=ws)
         torch.cuda.synchronize()
         check_zeroed_workspace(ws, big.wl.T)
+        # the second-digit histograms of the slice schedule follow the first-digit ones
+        first = (big.wl.T * 4 * 2048 * 4 + 255) // 256 * 256
+        h2 = ws[first:first + big.wl.T * 2048 * 4]
+        assert int(torch.count_nonzero(h2).item()) == 0, "second-digit histograms not left zero"
