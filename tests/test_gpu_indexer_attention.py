@@ -159,3 +159,29 @@ def test_workspace_shared_across_shapes():
         first = (big.wl.T * 4 * 2048 * 4 + 255) // 256 * 256
         h2 = ws[first:first + big.wl.T * 2048 * 4]
         assert int(torch.count_nonzero(h2).item()) == 0, "second-digit histograms not left zero"
+
+
+def test_ties_at_the_kth_key_without_overflow():
+    # every key row of each sequence repeated in runs of 8 (same codes and scale): each score
+    # appears 8 times, so the k-th largest is one of 8 equal keys and only some of them are kept
+    # (the lowest positions); the candidate lists stay within the first trip, so the slice
+    # schedule ranks the tied keys in its short list
+    g = Gpu(make(SMALL["ragged_i8"]))
+    for b in range(g.wl.B):
+        r0 = int(g.wl.kv_start[b])
+        n = int(g.wl.q_pos[g.wl.q_start[b + 1] - 1]) + 1
+        src = r0 + (torch.arange(n, device="cuda") // 8) * 8
+        g.k_cache[r0:r0 + n] = g.k_cache[src]
+        g.k_scale[r0:r0 + n] = g.k_scale[src]
+    idx = compare(g, False).cpu().numpy()
+    sc = g.scores().cpu().numpy()
+    k, ties = g.cfg.k, 0
+    for t in range(g.wl.T):
+        p = int(g.wl.q_pos[t])
+        if p + 1 <= k:
+            continue
+        row = sc[t, :p + 1]
+        kth = np.sort(row)[::-1][k - 1]
+        kept = np.count_nonzero(row[idx[t]] == kth)
+        ties += int(kept < np.count_nonzero(row == kth))
+    assert ties > 0, "no row had a partly kept tie at its k-th score"
