@@ -134,11 +134,19 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   // ahead of the MFMAs (issue kPre reads, then alternate one MFMA and one read): the MFMAs
   // run under the reads instead of after them.  Four independent accumulation chains (two per
   // key block) keep the matrix core's issue rate, not its latency, the limit.
+  // Addresses: chunk 4 ks + g of row r (r & 7 = c16 & 7) sits at chunk (4 ks + g) ^ (c16 & 7);
+  // for ks = 2 m + e that is byte 128 m + 64 (e ^ bit 2 of c16) + 16 (g ^ (c16 & 3)) of the row,
+  // so the 36 reads use four lane bases and immediate offsets (no per-read arithmetic).
+  const int sw = c16 & 7;
+  const int lb0 = 64 * ((sw >> 2) & 1) + 16 * (g ^ (sw & 3)), lb1 = lb0 ^ 64;
+  const unsigned char* kb0 = tile + c16 * kRowB;
+  const unsigned char* kb1 = tile + (16 + c16) * kRowB;
+  const unsigned char* kbase[2][2] = {{kb0 + lb0, kb0 + lb1}, {kb1 + lb0, kb1 + lb1}};
   v8bf kf[36];
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
-    kf[2 * ks] = *reinterpret_cast<const v8bf*>(tile + tile_off(c16, 4 * ks + g));
-    kf[2 * ks + 1] = *reinterpret_cast<const v8bf*>(tile + tile_off(16 + c16, 4 * ks + g));
+    kf[2 * ks] = *reinterpret_cast<const v8bf*>(kbase[0][ks & 1] + 128 * (ks >> 1));
+    kf[2 * ks + 1] = *reinterpret_cast<const v8bf*>(kbase[1][ks & 1] + 128 * (ks >> 1));
   }
   v4f sa[2][2];
 #pragma unroll
@@ -202,14 +210,22 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
   const lds_u8* tl = (const lds_u8*)tile;
   // V^T via ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 values of row
   // 8 g + j/4 (+4), columns d0 + 4 (j%4) .. +3; lane i receives the 4 rows of column d0 + i.
+  // Addresses: column block mb = 4 h + q of rows r0 = 8 g + c16 / 4 and r1 = r0 + 4 is chunk
+  // c = 16 ow + 2 mb + x (x = (c16 & 3) / 2) at (c ^ y) with y = r & 7, i.e. byte
+  // 256 ow + 128 h + 32 (q ^ y / 2) + 16 (x ^ (y & 1)) (+ 8 (c16 & 1) within the chunk): eight
+  // lane bases (row, q) and an immediate offset for h.
+  const int r0 = 8 * g + (c16 >> 2), y0 = c16 >> 2, y1 = y0 + 4, x = (c16 & 3) >> 1;
+  const lds_u8* vbase[2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    vbase[0][q] = tl + r0 * kRowB + 256 * ow + 32 * (q ^ (y0 >> 1)) + 16 * (x ^ (y0 & 1)) + 8 * (c16 & 1);
+    vbase[1][q] = tl + (r0 + 4) * kRowB + 256 * ow + 32 * (q ^ (y1 >> 1)) + 16 * (x ^ (y1 & 1)) + 8 * (c16 & 1);
+  }
   v4s lo[8], hi[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
-    const int col = 128 * ow + 16 * mb + 4 * (c16 & 3);
-    const int r0 = 8 * g + (c16 >> 2), r1 = r0 + 4;
-    const int c = col >> 3, wi = (col & 7) * 2;
-    lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r0, c) + wi));
-    hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tl + tile_off(r1, c) + wi));
+    lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[0][mb & 3] + 128 * (mb >> 2)));
+    hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[1][mb & 3] + 128 * (mb >> 2)));
   }
   v8bf pf[2];
 #pragma unroll
