@@ -119,7 +119,7 @@ constexpr int kPP = kKT * 2 + 16;        // P row pitch: 32 keys (a tile) + 16 B
 // Score wave, tile k: masked S^T blocks in the log2 domain and the softmax of tile k for heads
 // 16 hb .. +15.  Publishes P (bf16) and the rescale factor; updates the running max and sum.
 __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf* qf, const int* sidx,
-                                           int key0, int nkeys, float scale_log2, float& m_run,
+                                           int key0, float scale_log2, float& m_run,
                                            float& l_run, unsigned char* pt, float* alpha_out) {
   const int lane = threadIdx.x & 63, hb = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -165,33 +165,39 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 36 - (38 - kPre), 0);
   const v4f s0 = sa[0][0] + sa[0][1], s1 = sa[1][0] + sa[1][1];
-  // unused slots and keys past the split's end carry index -1 (the prologue pads the index
-  // stage to whole tiles)
+  // Raw scores; unused slots and keys past the split's end carry index -1 (the prologue pads the
+  // index stage to whole tiles) and are masked to -inf, in the tiles that hold any.  The scale
+  // (> 0) joins the exponent's argument in one FMA; the tile max of the raw scores times the
+  // scale is the max of the scaled scores.
   float z[2][4];
-  float m = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int ix[4] = {iv[kb].x, iv[kb].y, iv[kb].z, iv[kb].w};
-    const v4f sv = kb ? s1 : s0;
+  for (int e = 0; e < 4; ++e) { z[0][e] = s0[e]; z[1][e] = s1[e]; }
+  const int imin = min(min(min(iv[0].x, iv[0].y), min(iv[0].z, iv[0].w)),
+                       min(min(iv[1].x, iv[1].y), min(iv[1].z, iv[1].w)));
+  if (!__all(imin >= 0)) {                             // wave-uniform: a tile with unused slots
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      z[kb][e] = ix[e] >= 0 ? sv[e] * scale_log2 : -INFINITY;
-      m = fmaxf(m, z[kb][e]);
+    for (int kb = 0; kb < 2; ++kb) {
+      const int ix[4] = {iv[kb].x, iv[kb].y, iv[kb].z, iv[kb].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[kb][e] = ix[e] >= 0 ? z[kb][e] : -INFINITY;
     }
   }
-  const float tm = rows_max(m);
+  const float m = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+  const float tm = rows_max(m) * scale_log2;
   const bool move = (m_run == -INFINITY) ? (tm != -INFINITY) : (tm > m_run + kLazy);
   const float mnew = move ? tm : m_run;
   // v_exp_f32 directly: its arguments are <= kLazy, and -inf gives 0
   const float alpha = move ? __builtin_amdgcn_exp2f(m_run - tm) : 1.f;   // m_run = -inf: 0
-  const float mref = mnew == -INFINITY ? 0.f : mnew;   // all keys masked so far: every z is -inf
+  const float nref = mnew == -INFINITY ? 0.f : -mnew;  // all keys masked so far: every z is -inf
   float ps = 0.f;
   const int h = 16 * hb + c16;
+  auto p_of = [&](float zr) { return __builtin_amdgcn_exp2f(fmaf(zr, scale_log2, nref)); };
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     uint2 pk;
-    pk.x = pack_bf16x2(__builtin_amdgcn_exp2f(z[kb][0] - mref), __builtin_amdgcn_exp2f(z[kb][1] - mref));
-    pk.y = pack_bf16x2(__builtin_amdgcn_exp2f(z[kb][2] - mref), __builtin_amdgcn_exp2f(z[kb][3] - mref));
+    pk.x = pack_bf16x2(p_of(z[kb][0]), p_of(z[kb][1]));
+    pk.y = pack_bf16x2(p_of(z[kb][2]), p_of(z[kb][3]));
     // the sum uses the rounded values the value waves multiply with
     ps += (__uint_as_float(pk.x << 16) + __uint_as_float(pk.x & 0xFFFF0000u)) +
           (__uint_as_float(pk.y << 16) + __uint_as_float(pk.y & 0xFFFF0000u));
@@ -651,11 +657,13 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
       offs[it] = (uint32_t)ix * row_bytes + pcol[it];
     }
   };
+  // the LDS destinations are wave-uniform: scalar arithmetic from one base
+  const unsigned m0w = (unsigned)__builtin_amdgcn_readfirstlane((int)(ring_base + (wave - 2) * 1024));
   auto issue_tile = [&](int i) {
 #pragma unroll
     for (int it = 0; it < 18; ++it)
       asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(offs[it]), "s"(kv_seq),
-                   "{m0}"(ring_base + (i % kNBuf) * kTileB + ((wave - 2) + 2 * it) * 1024));
+                   "{m0}"(m0w + (unsigned)((i % kNBuf) * kTileB + it * 2048)));
   };
 
   // One loop per role, each with one barrier per step (nt + 1 steps), so that each role's
@@ -673,7 +681,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
     for (int k = 0; k <= nt; ++k) {
       lds_barrier();                                   // tile k landed; P of tile k - 1 consumed
       if (k < nt)
-        score_tile(ring + (k % kNBuf) * kTileB, qf, sidx, k * kKT, nkeys, a.scale_log2, m_run, l_run,
+        score_tile(ring + (k % kNBuf) * kTileB, qf, sidx, k * kKT, a.scale_log2, m_run, l_run,
                    pbuf[k & 1], abuf[k & 1]);
     }
     // running max and sum, per head, to the value waves
