@@ -264,13 +264,16 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
 // slice_loads issues the one memory round trip (before the workgroup's Q loads, so that waiting
 // for it does not wait for them); select_slice then works in LDS only, with LDS-only barriers.
 // `scr` is LDS scratch: 2 x 32 KiB of row bitmaps and 9 KiB of histogram and counters.  Rows
-// whose candidate lists overflow the first trip re-read the row's scores.  The select pass also
+// whose candidate lists overflow the first trip read every slot in a second trip (at most 16
+// chunks, no chunk beyond its slots), else re-read the row's scores.  The select pass also
 // counted the candidates' second digits per row (hist2): the second digit b2 is one scan of
 // those counts, and the k-th key is ranked among the few candidates in bin b2 by one wave
 // (a third histogram pass only when that bin holds more than 64 keys, or on overflow rows).
 // The slice ends in sidx, not yet behind a barrier.
 constexpr int kSelNT = 512;                            // threads of the attention workgroup
 constexpr int kSelLoad = kTkLoad / kSelNT;             // first-trip candidate entries per thread
+constexpr int kSelLoad2 = 16 * kTkCap / kSelNT;        // second trip: every slot of <= 16 chunks
+constexpr int kSelStream = 4;                          // chunks in flight when a row is re-read
 constexpr int kSelG = 4;                               // 16-byte bitmap groups per thread (<= 64 chunks)
 struct SliceIn {
   int p, sl, gpt;
@@ -343,10 +346,11 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
   uint32_t* kres = list + 64;                          // [4] K*, keys equal to it, ties kept
   if (tid < 64) {                                      // wave 0
     scnt[tid] = tid < nch ? in.my_cnt : 0u;            // tid < nch <= nch_m
-    // does any chunk's candidate list overflow the first trip?
-    const bool ov = tid < nch && (in.my_cnt >> 16) > (1u << sl);
-    const bool any_ov = __ballot(ov) != 0;
-    if (tid == 0) { *flag = any_ov; *n3 = 0u; }
+    // does any chunk's candidate list overflow the first trip (bit 0), or its slots (bit 1)?
+    const uint32_t nc = in.my_cnt >> 16;
+    const bool ov = tid < nch && nc > (1u << sl), ovc = tid < nch && nc > (uint32_t)kTkCap;
+    const uint32_t fl = (__ballot(ov) != 0 ? 1u : 0u) | (__ballot(ovc) != 0 ? 2u : 0u);
+    if (tid == 0) { *flag = fl; *n3 = 0u; }
   }
   // selects below are written as masks: a select between two arrays becomes a select of
   // addresses, which puts both in scratch memory
@@ -369,22 +373,51 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
 #pragma unroll
   for (int u = 0; u < kSelLoad; ++u)
     cvalid |= (uint32_t)((uint32_t)((tid + u * NT) & ((1 << sl) - 1)) < (cn[u] >> 16)) << u;
-  const bool streamed = *flag != 0u;
+  // Rows of at most 16 chunks whose lists fit their slots but not the first trip's share (a
+  // short row with a crowded digit) read every slot in a second trip; the rest re-read the row.
+  const uint32_t fl = *flag;
+  const bool streamed = (fl & 2u) != 0u || (fl != 0u && nch * kTkCap > kSelLoad2 * NT);
+  const bool second = fl != 0u && !streamed;
+  uint64_t ev2[kSelLoad2];
+  uint32_t cvalid2 = 0;
+  if (second) {                                        // block-uniform
+    const uint64_t* srow = a.tk_slots + (long)t * nch_m * kTkCap;
+#pragma unroll
+    for (int u = 0; u < kSelLoad2; ++u) {
+      const int f = tid + u * NT;                      // chunk f >> 9 < 16, slot f & 511
+      ev2[u] = srow[(long)min(f >> 9, nch_m - 1) * kTkCap + (f & (kTkCap - 1))];
+    }
+#pragma unroll
+    for (int u = 0; u < kSelLoad2; ++u) {
+      const int f = tid + u * NT;
+      cvalid2 |= (uint32_t)((uint32_t)(f & (kTkCap - 1)) < (scnt[f >> 9] >> 16)) << u;
+    }
+  }
   const uint32_t b1 = in.b1;
   const uint32_t need = (uint32_t)k - in.G;            // 1 <= need <= #candidates
   const float* row = a.scores + (long)t * a.ld;
   auto each_cand = [&](auto&& fn) {
-    if (!streamed) {
+    if (!streamed && !second) {
 #pragma unroll
       for (int u = 0; u < kSelLoad; ++u)
         if ((cvalid >> u) & 1u) fn((uint32_t)(in.ev[u] >> 32), (uint32_t)in.ev[u]);
-    } else {
-      for (int c = 0; c < nch; ++c) {
+    } else if (second) {
 #pragma unroll
-        for (int j = 0; j < kTkChunk / (4 * NT); ++j) {
-          const long e0 = (long)c * kTkChunk + 4 * (tid + NT * j);
-          const float4 x = *reinterpret_cast<const float4*>(row + min(e0, (a.ld & ~3L) - 4));
-          const float ff[4] = {x.x, x.y, x.z, x.w};
+      for (int u = 0; u < kSelLoad2; ++u)
+        if ((cvalid2 >> u) & 1u) fn((uint32_t)(ev2[u] >> 32), (uint32_t)ev2[u]);
+    } else {
+      constexpr int PER = kTkChunk / (4 * NT);         // float4 per thread per chunk
+      for (int c0 = 0; c0 < nch; c0 += kSelStream) {   // kSelStream chunks' loads in flight
+        float4 x[kSelStream * PER];
+#pragma unroll
+        for (int i = 0; i < kSelStream * PER; ++i) {
+          const long e0 = (long)(c0 + i / PER) * kTkChunk + 4 * (tid + NT * (i % PER));
+          x[i] = *reinterpret_cast<const float4*>(row + min(e0, (a.ld & ~3L) - 4));
+        }
+#pragma unroll
+        for (int i = 0; i < kSelStream * PER; ++i) {
+          const long e0 = (long)(c0 + i / PER) * kTkChunk + 4 * (tid + NT * (i % PER));
+          const float ff[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t key = order_key(ff[q]);

@@ -40,6 +40,9 @@ constexpr int kCW = kTkCW;           // bitmap words per chunk
 constexpr int kMaxLen = 64 * kChunk; // longest row
 constexpr int kCap = kTkCap;         // candidate slots per chunk
 constexpr int kLoadC = kTkLoad / kNT; // candidate entries per finalize thread (first trip)
+constexpr int kLoad2 = 2 * kLoadC;   // second trip: every slot of a row of up to 16 chunks
+static_assert(kLoad2 * kNT == 16 * kCap, "the second trip covers 16 chunks of kCap slots");
+constexpr int kStreamC = 4;          // chunks whose scores are in flight at once (streamed rows)
 constexpr int kRNT = 512;            // threads of a row workgroup (many-row batches)
 constexpr int kRNW = kRNT / 64;      // its waves
 constexpr int kRJ = 32;              // float4 slots per thread per segment
@@ -195,9 +198,11 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
 //  * The selection before this chunk: the earlier chunks' counts above b1, plus their
 //    candidates above K*, plus the ties at K* they keep.  This chunk's own selection (bitmap
 //    words, its candidates above K*, its kept ties) is written from there in position order.
-// Rows whose candidate lists are longer than the first trip loads (crowded digits, massive
-// ties) take their candidates from the row's scores instead.  Chunk 0 writes short rows and
-// zeroes the row's histogram shards for the next call.
+// Rows whose candidate lists are longer than the first trip loads take a second trip over
+// every slot when the row has at most 16 chunks and no chunk overflowed its slots (a short row
+// with a crowded digit); otherwise (massive ties, near-constant scores) they take their
+// candidates from the row's scores, kStreamC chunks in flight at a time.  Chunk 0 writes short
+// rows and zeroes the row's histogram shards for the next call.
 __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t sh[kNT / 64];
@@ -231,7 +236,7 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   int sl = 31 - __clz((kLoadC * kNT) / nch_m);
   sl = min(sl, 9);                                        // kCap = 512
   const uint64_t* srow = a.slots + (long)t * nch_m * kCap;
-  uint64_t ev[kLoadC];
+  uint64_t ev[kLoad2];                                    // [kLoadC, kLoad2): second trip only
 #pragma unroll
   for (int u = 0; u < kLoadC; ++u) {
     const int f = tid + u * kNT;
@@ -257,7 +262,8 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   if (tid < kCW) { bw[tid] = gw; tw[tid] = 0u; }
   if (tid < 4) red[tid] = 0u;
   __syncthreads();
-  if (tid < nch && (my_cnt >> 16) > (1u << sl)) flag = 1u;
+  // bit 0: a chunk holds more candidates than the first trip read; bit 1: more than its slots
+  if (tid < nch && (my_cnt >> 16) > (1u << sl)) atomicOr(&flag, (my_cnt >> 16) > (uint32_t)kCap ? 3u : 1u);
   // candidate validity without branches: every count read first (chunk f >> sl <= 63, as
   // 2^sl >= 64 for rows of at most 64 chunks; chunks past the row read 0)
   uint32_t cn[kLoadC];
@@ -268,23 +274,45 @@ __global__ void __launch_bounds__(kNT) topk_finalize(TkArgs a) {
   for (int u = 0; u < kLoadC; ++u)
     cvalid |= (uint32_t)((uint32_t)((tid + u * kNT) & ((1 << sl) - 1)) < (cn[u] >> 16)) << u;
   __syncthreads();                                        // flag
-  const bool streamed = flag != 0u;
+  const uint32_t fl = flag;
+  // Rows of at most 16 chunks whose lists fit their slots but not the first trip's share (a
+  // short row with a crowded digit) read every slot in a second trip; the rest stream the row.
+  const bool streamed = (fl & 2u) != 0u || (fl != 0u && nch * kCap > kLoad2 * kNT);
+  if (fl != 0u && !streamed) {                            // block-uniform
+#pragma unroll
+    for (int u = 0; u < kLoad2; ++u) {
+      const int f = tid + u * kNT;                        // chunk f >> 9 < 16, slot f & 511
+      ev[u] = srow[(long)min(f >> 9, nch_m - 1) * kCap + (f & (kCap - 1))];
+    }
+    cvalid = 0;
+#pragma unroll
+    for (int u = 0; u < kLoad2; ++u) {
+      const int f = tid + u * kNT;
+      cvalid |= (uint32_t)((uint32_t)(f & (kCap - 1)) < (scnt[f >> 9] >> 16)) << u;
+    }
+  }
   const uint32_t need = (uint32_t)k - G;                  // 1 <= need <= #candidates
   // every candidate of the row: from the first trip, or from the row's scores
   auto each_cand = [&](auto&& fn) {
     if (!streamed) {
 #pragma unroll
-      for (int u = 0; u < kLoadC; ++u)
+      for (int u = 0; u < kLoad2; ++u)
         if ((cvalid >> u) & 1u) fn((uint32_t)(ev[u] >> 32), (uint32_t)ev[u]);
     } else {
-      for (int c = 0; c < nch; ++c) {
-        const float4 x = load4(row, a.ld, c);
-        const float ff[4] = {x.x, x.y, x.z, x.w};
-        const int e0 = c * kChunk + 4 * tid;
+      for (int c0 = 0; c0 < nch; c0 += kStreamC) {      // kStreamC chunks' loads in flight
+        float4 x[kStreamC];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t key = order_key(ff[q]);
-          if (e0 + q <= p && (key >> 21) == b1) fn(key, (uint32_t)(e0 + q));
+        for (int j = 0; j < kStreamC; ++j) x[j] = load4(row, a.ld, min(c0 + j, nch - 1));
+#pragma unroll
+        for (int j = 0; j < kStreamC; ++j) {
+          if (c0 + j >= nch) break;
+          const float ff[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+          const int e0 = (c0 + j) * kChunk + 4 * tid;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t key = order_key(ff[q]);
+            if (e0 + q <= p && (key >> 21) == b1) fn(key, (uint32_t)(e0 + q));
+          }
         }
       }
     }

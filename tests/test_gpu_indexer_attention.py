@@ -185,3 +185,28 @@ def test_ties_at_the_kth_key_without_overflow():
         kept = np.count_nonzero(row[idx[t]] == kth)
         ties += int(kept < np.count_nonzero(row == kth))
     assert ties > 0, "no row had a partly kept tie at its k-th score"
+
+
+def test_crowded_threshold_digit():
+    # Every tenth key row of each sequence is a copy of one row with its scale raised 64x, and the
+    # head weights are made non-negative, so the copies hold every sequence's largest score.  The
+    # 40000-key sequence then has ~410 copies per 4096-score chunk, all in the threshold digit:
+    # more than the first trip reads per chunk at this cache length (256), within the chunk's
+    # slots (512), so both the finalize and the slice schedule take their second trip; its
+    # selection is the k lowest copy positions.  Every row is also checked against the oracle's
+    # top-k of the same scores.
+    import oracle
+    g = Gpu(make(Spec("crowded_digit", 7013, [40000, 20000, 6000], [1, 1, 1], k=2048, Hq=128)))
+    g.d["w"].abs_()
+    for b in range(g.wl.B):
+        r0 = int(g.wl.kv_start[b])
+        n = int(g.wl.q_pos[g.wl.q_start[b + 1] - 1]) + 1
+        dst = r0 + torch.arange(3, n, 10, device="cuda")
+        g.k_cache[dst] = g.k_cache[r0 + 3].clone()
+        g.k_scale[dst] = g.k_scale[r0 + 3].clone() * 64
+    idx = compare(g, False).cpu().numpy()
+    sc = g.scores().cpu().numpy()
+    k = g.cfg.k
+    assert np.array_equal(idx[0], 3 + 10 * np.arange(k)), "40000-key row: not the k lowest copies"
+    rows = [sc[t, :int(g.wl.q_pos[t]) + 1].astype(np.float64) for t in range(g.wl.T)]
+    assert np.array_equal(idx, oracle.topk_select(rows, k))

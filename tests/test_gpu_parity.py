@@ -97,12 +97,15 @@ def _topk_case(rng, T, L, k, kind):
         s = (-1.0 - np.abs(rng.standard_normal((T, L)))).astype(np.float32)
     elif kind == "zeros":         # +0 and -0 only
         s = np.where(rng.random((T, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
-    else:                         # narrow band: candidates crowd the threshold digit
+    elif kind == "narrow":        # narrow band: candidates overflow the chunks' slots
         s = (1000.0 + rng.random((T, L)) * 1e-3).astype(np.float32)
+    else:                         # crowded: a tenth of the keys in one digit (~410 per chunk)
+        s = np.where(rng.random((T, L)) < 0.1, 1.0 + 0.25 * rng.random((T, L)),
+                     1e-3 * rng.random((T, L))).astype(np.float32)
     return s
 
 
-@pytest.mark.parametrize("kind", ["random", "ties", "negative", "zeros", "narrow"])
+@pytest.mark.parametrize("kind", ["random", "ties", "negative", "zeros", "narrow", "crowded"])
 def test_topk_exact_on_identical_scores(rng, kind):
     """Same fp32 scores on both sides: the selected sets must be identical (ties -> lower
     positions), for long rows, rows shorter than k and rows of exactly k."""
