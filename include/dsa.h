@@ -346,8 +346,8 @@ dsa_status dsa_sparse_attn_decode_noalloc(const dsa_batch* batch, int32_t Hq, co
  * with the argument meanings, layouts and errors of those calls (flat caches only).  With a
  * prolog, H, D, code_dtype and scale_dtype must equal the prolog's.  Every argument is checked
  * before the first launch.
- * Schedule (chosen from the shapes; the results are identical): for at most 16 query tokens on
- * rows of at most 65536 positions the attention workgroups resolve their own slice of the
+ * Schedule (chosen from the shapes; the results are identical): for at most 32 query tokens on
+ * rows of at most 131072 positions the attention workgroups resolve their own slice of the
  * selection from the state the top-k's select pass leaves in the workspace (the k-th key of the
  * row by two more radix digits over the candidates, then their slots of the ascending
  * selection), which takes the top-k's separate finalize launch out of the step; idx is written

@@ -924,14 +924,15 @@ extern "C" dsa_status dsa_indexer_attention(const dsa_batch* bt, const dsa_dia* 
   const bool rows = bt->num_q >= dsa::kRowMinT;          // one workgroup per row: own histogram
   const bool fused_hist = !rows && bt->max_q_per_seq <= 4;
   // The attention resolves its own slices where that measured faster than the finalize launch
-  // it replaces: at most 16 query tokens on rows of at most 65536 positions (every attention
+  // it replaces: at most 32 query tokens on rows of at most 131072 positions (every attention
   // workgroup of a token repeats the row's k-th key search, whose cost grows with the row,
-  // while the finalize spreads it over the row's chunks).  DSA_DIA_SCHEDULE=slice|finalize
-  // forces one form (testing).
+  // while the finalize spreads it over the row's chunks; measured: faster for 8 tokens of 65536
+  // and 32 ragged ones of 6K-65K positions, equal for 8 of 131072).  DSA_DIA_SCHEDULE=
+  // slice|finalize forces one form (testing).
   // (The merge pass clears the second-digit histograms for the next call: the slice schedule
   // needs split partials, i.e. k > 32.)
   const bool splits = dsa_sparse_attn_workspace_size(bt->num_q, d->Hq, d->k) > 0;
-  bool slice = !rows && splits && bt->num_q <= 16 && bt->max_kv_len <= 65536;
+  bool slice = !rows && splits && bt->num_q <= 32 && bt->max_kv_len <= 131072;
   if (const char* e = getenv("DSA_DIA_SCHEDULE")) {
     if (!strcmp(e, "slice")) slice = !rows && splits;
     else if (!strcmp(e, "finalize")) slice = false;

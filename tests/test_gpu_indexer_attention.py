@@ -137,7 +137,7 @@ def test_all_equal_scores_take_the_lowest_positions():
         assert np.array_equal(idx[t, :keff], np.arange(keff)) and np.all(idx[t, keff:] == -1), t
 
 
-@pytest.mark.parametrize("n", [1, 4])
+@pytest.mark.parametrize("n", [1, 2, 4])
 def test_decode_workloads(n):
     g = Gpu(workloads.named(n))
     log(f"workload {n}: T={g.wl.T} B={g.wl.B}")
