@@ -273,7 +273,6 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
 constexpr int kSelNT = 512;                            // threads of the attention workgroup
 constexpr int kSelLoad = kTkLoad / kSelNT;             // first-trip candidate entries per thread
 constexpr int kSelLoad2 = 16 * kTkCap / kSelNT;        // second trip: every slot of <= 16 chunks
-constexpr int kSelStream = 4;                          // chunks in flight when a row is re-read
 constexpr int kSelG = 4;                               // 16-byte bitmap groups per thread (<= 64 chunks)
 struct SliceIn {
   int p, sl, gpt;
@@ -378,52 +377,74 @@ __device__ __forceinline__ void select_slice(const SfaArgs& a, const SliceIn& in
   const uint32_t fl = *flag;
   const bool streamed = (fl & 2u) != 0u || (fl != 0u && nch * kTkCap > kSelLoad2 * NT);
   const bool second = fl != 0u && !streamed;
-  uint64_t ev2[kSelLoad2];
+  // the entries: the first trip's in ev1; a second trip's first half replaces them, its second
+  // half in ev2
+  static_assert(kSelLoad2 == 2 * kSelLoad, "the second trip is two halves of the first's size");
+  uint64_t ev1[kSelLoad], ev2[kSelLoad];
+#pragma unroll
+  for (int u = 0; u < kSelLoad; ++u) ev1[u] = in.ev[u];
   uint32_t cvalid2 = 0;
   if (second) {                                        // block-uniform
     const uint64_t* srow = a.tk_slots + (long)t * nch_m * kTkCap;
 #pragma unroll
     for (int u = 0; u < kSelLoad2; ++u) {
       const int f = tid + u * NT;                      // chunk f >> 9 < 16, slot f & 511
-      ev2[u] = srow[(long)min(f >> 9, nch_m - 1) * kTkCap + (f & (kTkCap - 1))];
+      const uint64_t e = srow[(long)min(f >> 9, nch_m - 1) * kTkCap + (f & (kTkCap - 1))];
+      if (u < kSelLoad) ev1[u] = e; else ev2[u - kSelLoad] = e;
     }
+    cvalid = 0;
 #pragma unroll
     for (int u = 0; u < kSelLoad2; ++u) {
       const int f = tid + u * NT;
-      cvalid2 |= (uint32_t)((uint32_t)(f & (kTkCap - 1)) < (scnt[f >> 9] >> 16)) << u;
+      const uint32_t v = (uint32_t)((uint32_t)(f & (kTkCap - 1)) < (scnt[f >> 9] >> 16));
+      if (u < kSelLoad) cvalid |= v << u; else cvalid2 |= v << (u - kSelLoad);
     }
   }
   const uint32_t b1 = in.b1;
   const uint32_t need = (uint32_t)k - in.G;            // 1 <= need <= #candidates
   const float* row = a.scores + (long)t * a.ld;
   auto each_cand = [&](auto&& fn) {
-    if (!streamed && !second) {
+    if (!streamed) {
+      // one pass over the first trip's entries, two over the second trip's halves (one copy
+      // of fn; the halves are selected by value)
+#pragma unroll 1
+      for (int hf = 0; hf < (second ? 2 : 1); ++hf) {
+        const uint32_t cv = hf ? cvalid2 : cvalid;
 #pragma unroll
-      for (int u = 0; u < kSelLoad; ++u)
-        if ((cvalid >> u) & 1u) fn((uint32_t)(in.ev[u] >> 32), (uint32_t)in.ev[u]);
-    } else if (second) {
-#pragma unroll
-      for (int u = 0; u < kSelLoad2; ++u)
-        if ((cvalid2 >> u) & 1u) fn((uint32_t)(ev2[u] >> 32), (uint32_t)ev2[u]);
-    } else {
-      constexpr int PER = kTkChunk / (4 * NT);         // float4 per thread per chunk
-      for (int c0 = 0; c0 < nch; c0 += kSelStream) {   // kSelStream chunks' loads in flight
-        float4 x[kSelStream * PER];
-#pragma unroll
-        for (int i = 0; i < kSelStream * PER; ++i) {
-          const long e0 = (long)(c0 + i / PER) * kTkChunk + 4 * (tid + NT * (i % PER));
-          x[i] = *reinterpret_cast<const float4*>(row + min(e0, (a.ld & ~3L) - 4));
+        for (int u = 0; u < kSelLoad; ++u) {
+          const uint64_t e = hf ? ev2[u] : ev1[u];
+          if ((cv >> u) & 1u) fn((uint32_t)(e >> 32), (uint32_t)e);
         }
+      }
+    } else {
+      // the row's chunks in a rolled loop (little code: this path is rare) with the next
+      // chunk's loads in flight while one is processed
+      constexpr int PER = kTkChunk / (4 * NT);         // float4 per thread per chunk
+      auto load_chunk = [&](int c, float4 (&x)[PER]) {
 #pragma unroll
-        for (int i = 0; i < kSelStream * PER; ++i) {
-          const long e0 = (long)(c0 + i / PER) * kTkChunk + 4 * (tid + NT * (i % PER));
-          const float ff[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+        for (int j = 0; j < PER; ++j) {
+          const long e0 = (long)c * kTkChunk + 4 * (tid + NT * j);
+          x[j] = *reinterpret_cast<const float4*>(row + min(e0, (a.ld & ~3L) - 4));
+        }
+      };
+      float4 cur[PER];
+      load_chunk(0, cur);
+#pragma unroll 1
+      for (int c = 0; c < nch; ++c) {
+        float4 nxt[PER];
+        load_chunk(min(c + 1, nch - 1), nxt);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const long e0 = (long)c * kTkChunk + 4 * (tid + NT * j);
+          const float ff[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t key = order_key(ff[q]);
             if (e0 + q <= p && (key >> 21) == b1) fn(key, (uint32_t)(e0 + q));
           }
         }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) cur[j] = nxt[j];
       }
     }
   };
