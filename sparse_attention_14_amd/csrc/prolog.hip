@@ -29,11 +29,13 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
-// EPL = elements per lane (D / 64).  Lane l holds elements l*EPL .. l*EPL + EPL - 1.
-template <int EPL>
+// EPL = elements per lane (D / 64).  Lane l holds elements l*EPL .. l*EPL + EPL - 1.  BF16: the
+// input rows are bf16 (else fp32).
+template <int EPL, bool BF16>
 __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the wave's row, in scalar registers (every branch on it below is wave-uniform)
+  const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long nq_rows = (long)a.num_q * a.H;
   if (row >= nq_rows + a.num_k) return;
   const bool is_q = row < nq_rows;
@@ -42,24 +44,37 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
   const int D = EPL * 64;
   const void* src = is_q ? a.q_in : a.k_in;
 
-  double x[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const long off = r_in * D + lane * EPL + e;
-    x[e] = a.in_bf16 ? (double)bf16_to_f32(((const u16*)src)[off]) : (double)((const float*)src)[off];
+  // Every load of the row is issued before the first wait: its elements (raw bf16 or fp32 bits,
+  // one load per lane when the row is aligned for it), its rotary table entries and, for a key
+  // row, where it goes.
+  const long off = r_in * D + lane * EPL;
+  const bool wide = EPL == 2 && ((uintptr_t)src & (BF16 ? 3u : 7u)) == 0;   // wave-uniform
+  uint2 w = {0u, 0u};
+  if constexpr (BF16) {                                   // w.x = both elements (element 0 low)
+    if (wide) w.x = ((const uint32_t*)src)[off / 2];
+    else w.x = (uint32_t)((const u16*)src)[off] | (EPL == 2 ? (uint32_t)((const u16*)src)[off + EPL - 1] << 16 : 0u);
+  } else {
+    if (wide) w = ((const uint2*)src)[off / 2];
+    else {
+      w.x = ((const uint32_t*)src)[off];
+      if (EPL == 2) w.y = ((const uint32_t*)src)[off + EPL - 1];
+    }
   }
+  long drow = 0;                                          // destination row of a key row
+  if (!is_q) drow = a.k_slot ? a.k_slot[r_in] : a.kv_start[a.q_seq[r_in]] + a.q_pos[r_in];
 
   // RoPE on [rope_offset, rope_offset + rope_dim): partner of element i is i +- rope_dim/2
   // (or i ^ 1 when interleaved).  Products of fp32 values are exact in fp64, so each output
   // is rounded once.
-  if (a.rope_dim > 0) {
+  const bool rope = a.rope_dim > 0;
+  const int half = a.rope_dim >> 1;
+  int plane[EPL], pe[EPL];
+  bool first[EPL], in[EPL];
+  float cv[EPL], sv[EPL];
+  if (rope) {
     const float* cs = is_q ? a.q_cos : a.k_cos;
     const float* sn = is_q ? a.q_sin : a.k_sin;
-    const int half = a.rope_dim >> 1;
-    double pv[EPL];
     int pair[EPL];
-    bool first[EPL], in[EPL];
-    // gather every partner value before any element is rotated
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int i = lane * EPL + e;
@@ -73,21 +88,38 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
         pair[e] = first[e] ? rel : rel - half;
       }
       if (!in[e]) { partner = i; pair[e] = 0; }
-      const int plane = partner / EPL, pe = partner % EPL;
+      plane[e] = partner / EPL; pe[e] = partner % EPL;
+      cv[e] = cs[tab * half + pair[e]];                   // pair 0 for elements outside the range
+      sv[e] = sn[tab * half + pair[e]];
+    }
+  }
+  double x[EPL];
+  if constexpr (BF16) {
+    x[0] = (double)bf16_to_f32((u16)w.x);
+    if (EPL == 2) x[EPL - 1] = (double)bf16_to_f32((u16)(w.x >> 16));
+  } else {
+    x[0] = (double)__uint_as_float(w.x);
+    if (EPL == 2) x[EPL - 1] = (double)__uint_as_float(w.y);
+  }
+  if (rope) {
+    double pv[EPL];
+    // gather every partner value before any element is rotated
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
       pv[e] = 0.0;
 #pragma unroll
       for (int f = 0; f < EPL; ++f) {
-        const double v = __shfl(x[f], plane, kWave);
-        if (f == pe) pv[e] = v;
+        const double v = __shfl(x[f], plane[e], kWave);
+        if (f == pe[e]) pv[e] = v;
       }
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       if (in[e]) {
-        const double c = (double)cs[tab * half + pair[e]];
-        const double s = (double)sn[tab * half + pair[e]];
+        const double c = (double)cv[e];
+        const double sng = (double)sv[e];
         // first of the pair: x1 c - x2 s ; second: x2 c + x1 s
-        x[e] = first[e] ? x[e] * c - pv[e] * s : x[e] * c + pv[e] * s;
+        x[e] = first[e] ? x[e] * c - pv[e] * sng : x[e] * c + pv[e] * sng;
       }
     }
   }
@@ -148,13 +180,9 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
   }
 
   uint8_t* dst;
-  long drow;
   void* sdst;
   if (is_q) { dst = (uint8_t*)a.q_codes; drow = r_in; sdst = a.q_scale; }
-  else {
-    drow = a.k_slot ? a.k_slot[r_in] : a.kv_start[a.q_seq[r_in]] + a.q_pos[r_in];
-    dst = (uint8_t*)a.k_cache; sdst = a.k_scale;
-  }
+  else { dst = (uint8_t*)a.k_cache; sdst = a.k_scale; }
   if (EPL == 2) {
     const uint16_t v = (uint16_t)code[0] | ((uint16_t)code[EPL - 1] << 8);
     ((uint16_t*)(dst + drow * D))[lane] = v;
@@ -165,6 +193,16 @@ __global__ void __launch_bounds__(256) prolog_kernel(PrologArgs a) {
     if (a.scale_f16) ((u16*)sdst)[drow] = f32_to_f16_bits(s);
     else ((float*)sdst)[drow] = s;
   }
+}
+
+template <int EPL>
+static void launch_prolog_d(const PrologArgs& a, dim3 grid, hipStream_t st) {
+  if (a.in_bf16) hipLaunchKernelGGL((prolog_kernel<EPL, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((prolog_kernel<EPL, false>), grid, dim3(256), 0, st, a);
+}
+static void launch_prolog(int D, const PrologArgs& a, dim3 grid, hipStream_t st) {
+  if (D == 128) launch_prolog_d<2>(a, grid, st);
+  else launch_prolog_d<1>(a, grid, st);
 }
 
 }  // namespace dsa
@@ -218,8 +256,7 @@ extern "C" dsa_status dsa_indexer_prolog(const dsa_prolog_cfg* cfg, int32_t num_
   a.k_scale = k_scale;
   const dim3 grid((unsigned)((rows + 3) / 4));
   hipStream_t st = (hipStream_t)stream;
-  if (c.D == 128) hipLaunchKernelGGL(dsa::prolog_kernel<2>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(dsa::prolog_kernel<1>, grid, dim3(256), 0, st, a);
+  dsa::launch_prolog(c.D, a, grid, st);
   return dsa_host::check_launch("dsa_indexer_prolog");
 }
 
@@ -242,7 +279,6 @@ dsa_status dsa_prolog_own_keys(const dsa_prolog_cfg* cfg, const dsa_batch* bt, c
   a.k_scale = k_scale; a.q_seq = bt->q_seq; a.q_pos = bt->q_pos; a.kv_start = bt->kv_start;
   const dim3 grid((unsigned)((rows + 3) / 4));
   hipStream_t st = (hipStream_t)stream;
-  if (c.D == 128) hipLaunchKernelGGL(dsa::prolog_kernel<2>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(dsa::prolog_kernel<1>, grid, dim3(256), 0, st, a);
+  dsa::launch_prolog(c.D, a, grid, st);
   return DSA_OK;
 }
