@@ -24,6 +24,8 @@
 // A split writes its own softmax average O / l in bf16 with its running max and sum (fp32)
 // when the selection is spread over several workgroups; the combine kernel merges them in fp32
 // with the sink.  With one split the main kernel applies the sink and writes bf16 directly.
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "common.h"
@@ -118,9 +120,12 @@ constexpr int kPP = kKT * 2 + 16;        // P row pitch: 32 keys (a tile) + 16 B
 
 // Score wave, tile k: masked S^T blocks in the log2 domain and the softmax of tile k for heads
 // 16 hb .. +15.  Publishes P (bf16) and the rescale factor; updates the running max and sum.
+// BOUND: only the tile's first `valid` keys count (the index entries past them are not -1).
+template <bool BOUND = false>
 __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf* qf, const int* sidx,
                                            int key0, float scale_log2, float& m_run,
-                                           float& l_run, unsigned char* pt, float* alpha_out) {
+                                           float& l_run, unsigned char* pt, float* alpha_out,
+                                           int valid = kKT) {
   const int lane = threadIdx.x & 63, hb = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   // the keys' indices (-1 = unused slot), four per lane in one read; entries past nkeys are
@@ -174,12 +179,13 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   for (int e = 0; e < 4; ++e) { z[0][e] = s0[e]; z[1][e] = s1[e]; }
   const int imin = min(min(min(iv[0].x, iv[0].y), min(iv[0].z, iv[0].w)),
                        min(min(iv[1].x, iv[1].y), min(iv[1].z, iv[1].w)));
-  if (!__all(imin >= 0)) {                             // wave-uniform: a tile with unused slots
+  if (!__all(imin >= 0) || (BOUND && valid < kKT)) {   // wave-uniform: a tile with unused slots
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int ix[4] = {iv[kb].x, iv[kb].y, iv[kb].z, iv[kb].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[kb][e] = ix[e] >= 0 ? z[kb][e] : -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        z[kb][e] = ix[e] >= 0 && (!BOUND || 16 * kb + 4 * g + e < valid) ? z[kb][e] : -INFINITY;
     }
   }
   const float m = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
@@ -208,10 +214,12 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   if (g == 0) alpha_out[h] = alpha;
 }
 
-// Value wave, tile j: O^T[128 dims][32 heads] += V^T P^T with the rescale of tile j applied first.
-__device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* tile, const unsigned char* pt,
-                                           const float* alpha) {
-  const int lane = threadIdx.x & 63, ow = (threadIdx.x >> 6) - 4;
+// Value wave ow, tile j: O^T[128 dims][16 NB heads] += V^T P^T with the rescale of tile j applied
+// first.
+template <int NB = 2>
+__device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* tile, const unsigned char* pt,
+                                           const float* alpha, int ow) {
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const lds_u8* tl = (const lds_u8*)tile;
   // V^T via ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 values of row
@@ -233,21 +241,27 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[2], const unsigned char* t
     lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[0][mb & 3] + 128 * (mb >> 2)));
     hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[1][mb & 3] + 128 * (mb >> 2)));
   }
-  v8bf pf[2];
+  v8bf pf[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
     pf[nb] = *reinterpret_cast<const v8bf*>(pt + (16 * nb + c16) * kPP + (8 * g) * 2);
-  const float a0 = alpha[c16], a1 = alpha[16 + c16];
-  if (__any(a0 != 1.f || a1 != 1.f)) {               // wave-uniform, rare after the first tile
+  float al[NB];
+  bool rescale = false;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) { acc[mb][0] *= a0; acc[mb][1] *= a1; }
+  for (int nb = 0; nb < NB; ++nb) { al[nb] = alpha[16 * nb + c16]; rescale |= al[nb] != 1.f; }
+  if (__any(rescale)) {                                // wave-uniform, rare after the first tile
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= al[nb];
   }
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[mb][0], lo[mb][1], lo[mb][2], lo[mb][3],
                                                  hi[mb][0], hi[mb][1], hi[mb][2], hi[mb][3]});
-    acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0], acc[mb][0], 0, 0, 0);
-    acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1], acc[mb][1], 0, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc[mb][nb], 0, 0, 0);
   }
 }
 
@@ -771,7 +785,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   for (int k = 0; k <= nt; ++k) {
     lds_barrier();                                     // P of tile k - 1 published
     if (k >= 1)
-      value_tile(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1]);
+      value_tile(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1], wave - 4);
   }
   lds_barrier();                                       // running max and sum published
   const int ow = wave - 4;
@@ -823,6 +837,206 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   const int vt = tid - 256;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const int piece = vt + 256 * i, hl = piece >> 6, c = piece & 63;
+    if (h0 + hl < a.Hq)
+      *reinterpret_cast<uint4*>(obase + (long)hl * kDv + c * 8) =
+          *reinterpret_cast<const uint4*>(ot + hl * kOP + c * 16);
+  }
+}
+
+// Prefill-sized batches (one split per token, flat caches): one workgroup (8 waves) per token
+// and 64 query heads, so each gathered row serves twice the heads of sfa_kernel and the QK^T
+// MFMAs spread over all four SIMDs:
+//  * score waves 0-3, wave = 16 heads (score_tile as in sfa_kernel, one per SIMD);
+//  * value waves 4-7, wave = value dims 128 (w - 4) .. +127 for all 64 heads (value_tile over
+//    four head blocks), each also gathering 9 of the 36 1-KiB pieces of every tile (no loader
+//    waves: the 8 waves share the SIMDs two by two, so a value wave may take 256 VGPRs).
+// The 8 KiB index stage of sfa_kernel does not fit beside the larger P buffer: the selected
+// indices move through an 8-tile ring in LDS instead, each value wave bringing 8 indices of tile
+// k + 5 per step with one direct-to-LDS dword load (the first five tiles' from the prologue).
+// Tiles past the selection's end read clamped indices; score_tile masks them by count.
+// Results are bit-identical to sfa_kernel<true, false>: the same tiles, per-head arithmetic and
+// order.
+constexpr int kIR = 8;                                 // index ring: tiles
+__global__ void __launch_bounds__(512) sfa_kernel64(SfaArgs a) {
+  constexpr int NH = 64;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kNBuf * kTileB];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[2][NH * kPP];
+  __shared__ float abuf[2][NH];
+  __shared__ float fin[2][NH];
+  __shared__ __attribute__((aligned(16))) int sring[kIR * kKT];
+  if (a.poison) {
+    poison_lds(&ring, sizeof(ring));
+    poison_lds(&pbuf, sizeof(pbuf));
+    poison_lds(&abuf, sizeof(abuf));
+    poison_lds(&fin, sizeof(fin));
+    poison_lds(&sring, sizeof(sring));
+    __syncthreads();
+  }
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nwg = a.T * a.n_hg;                        // n_split == 1
+  const int lid = xcd_remap(blockIdx.x, nwg);
+  const int hg = lid % a.n_hg, t = lid / a.n_hg;
+  const int h0 = hg * NH;
+  const int nkeys = a.k;
+  const int nt = (nkeys + kKT - 1) / kKT;
+  const unsigned ring_base = (unsigned)(uintptr_t)(lds_u8*)ring;
+  const unsigned sring_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)sring;
+  // ---- prologue: Q (64 heads x 1152 B, laid out like a tile) into ring slots 2-3, the first
+  // five tiles' indices into the index ring, the token's sequence and its first cache row
+  {
+    const u16* qbase = uniform_ptr(a.q + (long)t * a.Hq * kDqk);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int it = 0; it < 2 * kTileB / 1024 / 8; ++it) {   // 72 pieces of 1 KiB, 9 per wave
+      const int j = wave + 8 * it;
+      const int o = j * 1024 + ln * 16;
+      const int r = o / kRowB;
+      const int c = ((o % kRowB) >> 4) ^ (r & 7);
+      const uint32_t off = (uint32_t)min(h0 + r, a.Hq - 1) * (uint32_t)kRowB + (uint32_t)c * 16u;
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(qbase),
+                   "{m0}"(ring_base + 2 * kTileB + j * 1024));
+    }
+  }
+  const int32_t* irow = a.idx + (long)t * a.k;
+  int32_t iv0 = 0;
+  if (tid < 5 * kKT) iv0 = irow[min(tid, nkeys - 1)];  // tiles 0-4 (clamped past the selection)
+  const long kv_lane = a.kv_start[min(lane, a.B - 1)];
+  asm volatile("" ::: "memory");                       // keep the loads above issued here
+  const int seq = a.q_seq[t];
+  if (tid < 5 * kKT) sring[tid] = iv0;
+  long kv0;
+  if (a.B <= 64) {
+    kv0 = (long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kv_lane >> 32), seq) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)kv_lane, seq));
+  } else {
+    kv0 = a.kv_start[seq];
+  }
+  const u16* kv_seq = uniform_ptr(a.kv + kv0 * a.kv_stride);
+  const uint32_t row_bytes = (uint32_t)a.kv_stride * 2u;
+  retire(kv_lane);
+  wait_vm<0>();                                        // this wave's Q loads have landed
+  lds_barrier();                                       // Q and the first indices visible
+
+  if (wave < 4) {
+    // ---- score waves
+    v8bf qf[18];                                       // Q of heads 16 wave + c16
+    float m_run = -INFINITY, l_run = 0.f;
+    const int r = 16 * wave + c16;
+    const unsigned char* qt = ring + 2 * kTileB;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      qf[ks] = *reinterpret_cast<const v8bf*>(qt + tile_off(r, 4 * ks + g));
+      if (h0 + r >= a.Hq) qf[ks] = v8bf{};
+    }
+    for (int k = 0; k <= nt; ++k) {
+      lds_barrier();                                   // tile k landed; P of tile k - 1 consumed
+      if (k < nt)
+        score_tile<true>(ring + (k % kNBuf) * kTileB, qf, sring + (k % kIR) * kKT, 0, a.scale_log2,
+                         m_run, l_run, pbuf[k & 1], abuf[k & 1], nkeys - k * kKT);
+    }
+    if (g == 0) {
+      fin[0][r] = m_run;
+      fin[1][r] = l_run;
+    }
+    lds_barrier();
+    return;
+  }
+  // ---- value waves, also the gatherers: pieces J = ow + 4 it (it < 9) of every tile
+  const int ow = wave - 4;
+  uint32_t offs[9], prow[9], pcol[9];
+#pragma unroll
+  for (int it = 0; it < 9; ++it) {
+    const int o = (ow + 4 * it) * 1024 + lane * 16;
+    const int r = o / kRowB;
+    prow[it] = (uint32_t)r;
+    pcol[it] = (uint32_t)((((o % kRowB) >> 4) ^ (r & 7)) << 4);
+  }
+  auto tile_offsets = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < 9; ++it) {
+      const int ix = max(sring[(i % kIR) * kKT + (int)prow[it]], 0);
+      offs[it] = (uint32_t)ix * row_bytes + pcol[it];
+    }
+  };
+  const unsigned m0w = (unsigned)__builtin_amdgcn_readfirstlane((int)(ring_base + ow * 1024));
+  auto issue_tile = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < 9; ++it)
+      asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(offs[it]), "s"(kv_seq),
+                   "{m0}"(m0w + (unsigned)((i % kNBuf) * kTileB + it * 4096)));
+  };
+  // indices 8 ow .. + 7 of tile i into the index ring (lanes 0-7; clamped past the selection;
+  // issued for every step, past the last tile too, into a slot no one reads any more)
+  const int32_t* ibase = uniform_ptr(irow);
+  auto issue_idx = [&](int i) {
+    if (lane < 8) {
+      const uint32_t off = (uint32_t)min(i * kKT + 8 * ow + lane, nkeys - 1) * 4u;
+      asm volatile("global_load_lds_dword %0, %1" :: "v"(off), "s"(ibase),
+                   "{m0}"((unsigned)__builtin_amdgcn_readfirstlane(
+                       (int)(sring_base + (unsigned)(((i % kIR) * kKT + 8 * ow) * 4)))));
+    }
+  };
+  tile_offsets(0);
+  issue_tile(0);
+  if (nt > 1) { tile_offsets(1); issue_tile(1); }
+  if (nt > 2) tile_offsets(2);
+  v4f acc[8][4];                                       // O^T
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k <= nt; ++k) {
+    // tile k landed: issued after it are (k >= 1) the index load of step k - 1 and tile k + 1
+    if (k < nt) {
+      if (k == 0) { if (nt > 1) wait_vm<9>(); else wait_vm<0>(); }
+      else if (k + 1 < nt) wait_vm<10>();
+      else wait_vm<1>();
+    }
+    lds_barrier();
+    issue_idx(k + 5);                                  // the indices before the tile: see above
+    if (k + 2 < nt) {                                  // into the slot of tile k - 2
+      issue_tile(k + 2);
+      if (k + 3 < nt) tile_offsets(k + 3);             // its indices came with tile k or earlier
+    }
+    if (k >= 1)
+      value_tile<4>(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1], ow);
+  }
+  wait_vm<0>();                                        // the index loads past the end
+  lds_barrier();                                       // running max and sum published
+
+  // ---- epilogue (FINAL): rows through ring slots 0-1 as in sfa_kernel, 64 heads
+  constexpr int kOP = kDv * 2 + 16;
+  static_assert(NH * kOP <= 2 * kTileB, "the output rows do not fit two ring slots");
+  unsigned char* ot = ring;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int hl = 16 * nb + c16;
+    const int h = h0 + hl;
+    if (h >= a.Hq) continue;
+    const float mh = fin[0][hl], lh = fin[1][hl];
+    const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float M = fmaxf(mh, sk);
+    const float f = mh == -INFINITY ? 0.f : exp2f(mh - M);
+    const float den = lh * f + (sk == -INFINITY ? 0.f : exp2f(sk - M));
+    const float inv = den > 0.f ? f / den : 0.f;
+    unsigned char* orow = ot + hl * kOP + (128 * ow + 4 * g) * 2;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[mb][nb][0] * inv, acc[mb][nb][1] * inv);
+      pk.y = pack_bf16x2(acc[mb][nb][2] * inv, acc[mb][nb][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * mb) = pk;
+    }
+  }
+  lds_barrier();
+  // 64 rows x 64 pieces of 16 bytes over the 256 value-wave threads; row hl = piece / 64
+  u16* obase = a.out + ((long)t * a.Hq + h0) * kDv;
+  const int vt = tid - 256;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
     const int piece = vt + 256 * i, hl = piece >> 6, c = piece & 63;
     if (h0 + hl < a.Hq)
       *reinterpret_cast<uint4*>(obase + (long)hl * kDv + c * 8) =
@@ -889,7 +1103,7 @@ __global__ void __launch_bounds__(256) sfa_combine(SfaArgs a) {
   *reinterpret_cast<uint4*>(a.out + ((long)t * a.Hq + h) * kDv + lane * 8) = pk;
 }
 
-struct SfaPlan { int n_hg, n_split, kps; };
+struct SfaPlan { int n_hg, n_split, kps; bool h64; };
 
 // One workgroup per CU (the LDS ring takes ~150 KiB): aim for 256 workgroups.
 static SfaPlan plan(int T, int Hq, int k) {
@@ -905,7 +1119,19 @@ static SfaPlan plan(int T, int Hq, int k) {
   kps = (kps + kKT - 1) / kKT * kKT;
   p.kps = kps;
   p.n_split = (k + kps - 1) / kps;
+  p.h64 = false;
   return p;
+}
+
+// Prefill-sized batches on flat caches (one split per token, at least 256 workgroups of 64
+// heads): sfa_kernel64.  DSA_SFA_H64=0 keeps sfa_kernel (testing).
+static void plan_h64(SfaPlan& p, int T, int Hq, bool flat) {
+  const char* e = getenv("DSA_SFA_H64");
+  const bool off = e && !strcmp(e, "0");
+  if (flat && !off && p.n_split == 1 && Hq % 64 == 0 && (long)T * (Hq / 64) >= 256) {
+    p.h64 = true;
+    p.n_hg = Hq / 64;
+  }
 }
 
 }  // namespace dsa
@@ -978,7 +1204,8 @@ static dsa_status sfa_prepare(const dsa_batch* bt, int32_t Hq, const void* q, co
   if (sel && (pg || !sel->scores || !sel->hist2 || sel->nch < 1 || sel->nch > 64))
     return fail(DSA_ERR_UNSUPPORTED, "%s: a pending selection needs flat caches and rows of at most 64 chunks", fn);
   if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)out) & 15) return fail(DSA_ERR_INVALID_ARG, "%s: q/kv/out must be 16-byte aligned", fn);
-  const dsa::SfaPlan p = dsa::plan(bt->num_q, Hq, k);
+  dsa::SfaPlan p = dsa::plan(bt->num_q, Hq, k);
+  dsa::plan_h64(p, bt->num_q, Hq, !pg && !sel);
   if (sel && p.n_split < 2)                              // the merge clears the second-digit histograms
     return fail(DSA_ERR_UNSUPPORTED, "%s: a pending selection needs split partials (k > 32)", fn);
   const size_t need = dsa_sparse_attn_workspace_size(bt->num_q, Hq, k);
@@ -1019,6 +1246,8 @@ static void sfa_launch_split(const dsa::SfaArgs& a, const dsa::SfaPlan& p, hipSt
   }
   if (a.tk_bg)                                           // the kernel resolves its own slice
     hipLaunchKernelGGL((dsa::sfa_kernel<false, true>), grid, dim3(512), 0, s, a);   // n_split > 1
+  else if (p.h64)                                        // n_split == 1, flat
+    hipLaunchKernelGGL(dsa::sfa_kernel64, grid, dim3(512), 0, s, a);
   else if (p.n_split == 1)
     hipLaunchKernelGGL((dsa::sfa_kernel<true, false>), grid, dim3(512), 0, s, a);
   else

@@ -4,6 +4,8 @@ Small cases span several tiles with ragged tails and hit each edge the method ha
 with -1 padding, exact ties, empty selections, no sink, fp8 with RoPE+Hadamard, many tokens
 per sequence); the named full-size workloads run the launch configuration the benchmark uses.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -173,6 +175,36 @@ def test_sparse_attention_isolated(rng, Hq, T, sink, pad):
     check_sfa(out, ref)
     if T >= 3:
         assert not out[1].float().abs().sum().item()
+
+
+@pytest.mark.parametrize("T,k,pad", [(256, 2048, 0.2), (300, 100, 0.0), (257, 32, 0.5), (512, 200, 0.1)])
+def test_sparse_attention_64_head_kernel_equals_32_head_kernel(rng, T, k, pad):
+    """Batches with one split per token run the 64-head kernel (index ring in LDS, value waves that
+    also gather); it must reproduce the 32-head kernel bit for bit -- the same tiles, per-head
+    arithmetic and order -- on random selections with -1 holes, empty selections, a partial last
+    tile (k = 100), a single tile (k = 32) and fewer tiles than the prologue stages (k < 160),
+    and match the oracle."""
+    lens = list(rng.integers(300, 5000, size=T))
+    sp = Spec(f"sfa64_{T}_{k}", 7400 + T + k, lens, [1] * T, H=8, D=64, k=k, Hq=128)
+    wl = make(sp)
+    idx = workloads.random_topk_idx(rng, wl.q_pos, k, pad_frac=pad)
+    idx[1, :] = -1                                       # an empty selection
+    log(f"case sfa64 T={T} k={k} pad={pad}")
+    d = workloads.device_arrays(wl)
+    batch = dsa.make_batch(wl.q_start, wl.q_seq, wl.q_pos, wl.kv_start)
+    it = torch.from_numpy(idx).cuda()
+    out64 = dsa.dsa_sparse_attn_decode(batch, d["q"], d["kv"], it, d["sink"], wl.scale)
+    os.environ["DSA_SFA_H64"] = "0"
+    try:
+        out32 = dsa.dsa_sparse_attn_decode(batch, d["q"], d["kv"], it, d["sink"], wl.scale)
+    finally:
+        os.environ.pop("DSA_SFA_H64", None)
+    torch.cuda.synchronize()
+    assert torch.equal(out64, out32), "64-head kernel differs from the 32-head kernel"
+    sample = np.arange(0, T, 7)
+    ref = oracle.sparse_attention(wl.q[sample], wl.kv, idx[sample], np.asarray(wl.q_seq)[sample], wl.kv_start,
+                                  wl.sink, wl.scale)
+    check_sfa(out64[torch.from_numpy(sample).cuda()], ref)
 
 
 @pytest.mark.parametrize("Hq,T", [(128, 8), (16, 3), (128, 600)])
