@@ -367,10 +367,18 @@ def main():
     # flops), where the keys and gathered rows come from the caches
     prefill = wl.max_q_per_seq > 4
     idx_peak = INT8_PEAK_TOPS if cfg.code == "i8" else BF16_PEAK_TFLOPS
-    # decode batches (at most 4 query tokens per sequence) take the streaming indexer kernel
-    idx_kernel = "dsa::indexer_stream_kernel" if wl.max_q_per_seq <= 4 else "dsa::indexer_kernel"
+    # decode batches (at most 4 query tokens per sequence) take the streaming indexer kernel,
+    # int8 prefill of the 64 x 128 shape the prefill kernel; batches with one attention split
+    # per token and at least 256 workgroups of 64 heads the 64-head attention kernel
+    if wl.max_q_per_seq <= 4:
+        idx_kernel = "dsa::indexer_stream_kernel"
+    elif cfg.code == "i8" and cfg.H == 64 and cfg.D == 128:
+        idx_kernel = "dsa::indexer_prefill_kernel"
+    else:
+        idx_kernel = "dsa::indexer_kernel"
+    sfa_kernel = "dsa::sfa_kernel64" if Hq % 64 == 0 and T * (Hq // 64) >= 256 else "dsa::sfa_kernel"
     single = {"indexer": (idx_kernel, b_indexer, idx_ops, idx_peak),
-              "sfa_split": ("dsa::sfa_kernel", n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4,
+              "sfa_split": (sfa_kernel, n_sel * 1152 + T * Hq * 576 * 2 + T * k * 4,
                             sfa_flops, BF16_PEAK_TFLOPS)}
     dominant = max(single, key=lambda n: stage_us[n])
     kernel_name, dom_bytes, dom_ops, dom_peak = single[dominant]
