@@ -126,6 +126,28 @@ def test_topk_exact_on_identical_scores(rng, kind):
     assert np.array_equal(idx, ref)
 
 
+@pytest.mark.parametrize("kind", ["random", "ties", "negative", "zeros", "narrow", "crowded"])
+def test_row_topk_exact_on_identical_scores(rng, kind):
+    """Batches of 256 or more rows take one workgroup per row (its own first-digit histogram, the
+    keys at or above the threshold digit compacted in LDS in position order, or re-read from the
+    scores when they do not fit).  Same fp32 scores on both sides: the selected sets must be
+    identical (ties -> lower positions), for rows of one to three 65536-score segments, rows
+    shorter than k and rows of exactly k."""
+    T, k = 256, 2048
+    lens = rng.integers(2049, 140000, size=T)
+    lens[:8] = [2048, 2047, 100, 2049, 65536, 65537, 131072, 140000]
+    L = int(lens.max())
+    s = _topk_case(rng, T, L, k, kind)
+    ld = (L + 63) // 64 * 64
+    sc = np.zeros((T, ld), dtype=np.float32)
+    sc[:, :L] = s
+    batch = dsa.make_batch(np.arange(T + 1), np.arange(T), lens - 1, np.zeros(T))
+    log(f"case row topk {kind}")
+    idx = dsa.dsa_topk(batch, torch.from_numpy(sc).cuda(), k).cpu().numpy()
+    rows = [sc[t, :lens[t]].astype(np.float64) for t in range(T)]
+    assert np.array_equal(idx, oracle.topk_select(rows, k))
+
+
 def test_indexer_topk_all_ties_take_lowest_positions():
     """Every score equal (zero head weights): every key of a row is in the threshold digit, so the
     row workgroup's ordered list holds the whole row (9000 and 2100 keys) or overflows it (70000
