@@ -497,9 +497,9 @@ __device__ __forceinline__ float add_half_swap(float v) {
 // per head over the chunk's tokens and the cached keys, then ReLU and the head-weighted sum.
 //
 // Workgroup = (sequence, tile of kPT query tokens).  The tile's query codes and w * q_scale stay
-// in LDS; its eight waves split the keys the tile sees into kPG-key groups (wave w takes groups
-// w, w + 8, ...).  A wave holds one group's key codes in registers, loaded straight from memory
-// with the next group's loads in flight, and runs every token of the tile against them:
+// in LDS; its kPW waves split the keys the tile sees into kPG-key groups (wave w takes groups
+// w, w + kPW, ...).  A wave holds one group's key codes in registers, loaded straight from memory,
+// and runs every token of the tile against them:
 // 16 v_mfma_i32_32x32x32_i8 per token (2 head blocks x 2 key blocks x 4 depth steps, query
 // fragments from LDS), then the ReLU-weighted head sum (3 VALU ops per (token, head, key) --
 // the kernel's bound) and the key scale.  Each key group is read once per kPT tokens (the
@@ -507,15 +507,18 @@ __device__ __forceinline__ float add_half_swap(float v) {
 // position (wave-uniform) and masks the keys past it inside the last one.
 constexpr int kPT = 16;                        // query tokens per prefill workgroup
 constexpr int kPG = 64;                        // keys per wave group
-constexpr int kPW = 12;                        // waves per prefill workgroup (3 per SIMD)
+constexpr int kPW = 16;                        // waves per prefill workgroup (4 per SIMD)
+constexpr int kQP = 144;                       // LDS bytes per staged query row (128 + 16)
 
 __global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
   constexpr int H = 64, D = 128;
-  __shared__ __attribute__((aligned(16))) uint8_t qs[kPT * H * D];       // 128 KiB
-  __shared__ __attribute__((aligned(16))) float wq[kPT][H];
+  // one LDS block: w * q_scale first, then the query codes, so that every read below is a
+  // per-lane base plus an immediate offset (the offset field reaches 64 KiB)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kPT * H * 4 + kPT * H * kQP];
+  float (*wq)[H] = reinterpret_cast<float (*)[H]>(lds);
+  uint8_t* qs = lds + kPT * H * 4;
   if (a.poison) {
-    poison_lds(&qs, sizeof(qs));
-    poison_lds(&wq, sizeof(wq));
+    poison_lds(&lds, sizeof(lds));
     __syncthreads();
   }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -532,11 +535,11 @@ __global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) maxp = max(maxp, __shfl_xor(maxp, m, kWave));
   const long kv0 = a.bt ? 0 : a.kv_start[b];               // paged: rows through the block table
-  // stage the tile's query codes (row r's 16-byte chunk c at chunk c ^ (r % 8): the 32 rows one
-  // fragment read touches then spread over all banks) and head weights
+  // stage the tile's query codes (rows kQP = 144 bytes apart: the 32 rows one fragment read
+  // touches start 36 banks apart and cover all 64 banks) and head weights
   for (int o = tid * 16; o < nt * H * D; o += kPW * 64 * 16) {
     const int r = o >> 7, c = (o >> 4) & 7;
-    *reinterpret_cast<uint4*>(qs + r * D + ((c ^ (r & 7)) << 4)) =
+    *reinterpret_cast<uint4*>(qs + r * kQP + (c << 4)) =
         *reinterpret_cast<const uint4*>(a.q_codes + (long)t0 * H * D + o);
   }
   for (int i = tid; i < nt * H; i += kPW * 64) {
@@ -565,27 +568,22 @@ __global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        qf[mb][q] = *reinterpret_cast<const v4i*>(qs + (j * H + 32 * mb + col) * D +
-                                                  (((2 * q + hv) ^ (col & 7)) << 4));
+        qf[mb][q] = *reinterpret_cast<const v4i*>(qs + (j * H + 32 * mb + col) * kQP +
+                                                  ((2 * q + hv) << 4));
   };
-  v4i kf[2][4], kn[2][4];
-  float ks[2], ksn[2];
-  if (wave < ngroups) load_group(wave, kn, ksn);
+  // a wave loads its group at the group's start: the other three waves of its SIMD run their
+  // tokens meanwhile (a register copy of the next group in flight would cost the fourth wave)
+  v4i kf[2][4];
+  float ks[2];
   for (int g = wave; g < ngroups; g += kPW) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      ks[kb] = ksn[kb];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) kf[kb][q] = kn[kb][q];
-    }
-    if (g + kPW < ngroups) load_group(g + kPW, kn, ksn);     // in flight under this group's tokens
+    load_group(g, kf, ks);
     const int key0 = g * kPG;
     for (int j = 0; j < nt; ++j) {
       const int p = __builtin_amdgcn_readlane(pl, j);
       if (key0 > p) continue;
       v4i qa[2][4];
       load_q(j, qa);
-      float sum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      float sum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};           // two partial sums per key block
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         v16i acc0 = {}, acc1 = {};
@@ -600,13 +598,13 @@ __global__ void __launch_bounds__(kPW * 64) indexer_prefill_kernel(IdxArgs a) {
           const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sum[0][r] = fmaf(wv[r], (float)max(acc0[4 * i + r], 0), sum[0][r]);
-            sum[1][r] = fmaf(wv[r], (float)max(acc1[4 * i + r], 0), sum[1][r]);
+            sum[0][r & 1] = fmaf(wv[r], (float)max(acc0[4 * i + r], 0), sum[0][r & 1]);
+            sum[1][r & 1] = fmaf(wv[r], (float)max(acc1[4 * i + r], 0), sum[1][r & 1]);
           }
         }
       }
-      const float s0v = add_half_swap((sum[0][0] + sum[0][1]) + (sum[0][2] + sum[0][3]));
-      const float s1v = add_half_swap((sum[1][0] + sum[1][1]) + (sum[1][2] + sum[1][3]));
+      const float s0v = add_half_swap(sum[0][0] + sum[0][1]);
+      const float s1v = add_half_swap(sum[1][0] + sum[1][1]);
       if (hv == 0) {
         float* dst = a.scores + (long)(t0 + j) * a.ld;
         const int k0 = key0 + col, k1 = key0 + 32 + col;
