@@ -214,11 +214,9 @@ __device__ __forceinline__ void score_tile(const unsigned char* tile, const v8bf
   if (g == 0) alpha_out[h] = alpha;
 }
 
-// Value wave ow, tile j: O^T[128 dims][16 NB heads] += V^T P^T with the rescale of tile j applied
-// first.
-template <int NB = 2>
-__device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* tile, const unsigned char* pt,
-                                           const float* alpha, int ow) {
+// Value wave ow: its V^T fragments of one tile (value dims 128 ow .. +127, the tile's 32 keys).
+struct VFrag { v4s lo[8], hi[8]; };
+__device__ __forceinline__ VFrag value_read(const unsigned char* tile, int ow) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const lds_u8* tl = (const lds_u8*)tile;
@@ -235,12 +233,22 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* 
     vbase[0][q] = tl + r0 * kRowB + 256 * ow + 32 * (q ^ (y0 >> 1)) + 16 * (x ^ (y0 & 1)) + 8 * (c16 & 1);
     vbase[1][q] = tl + (r0 + 4) * kRowB + 256 * ow + 32 * (q ^ (y1 >> 1)) + 16 * (x ^ (y1 & 1)) + 8 * (c16 & 1);
   }
-  v4s lo[8], hi[8];
+  VFrag v;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
-    lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[0][mb & 3] + 128 * (mb >> 2)));
-    hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[1][mb & 3] + 128 * (mb >> 2)));
+    v.lo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[0][mb & 3] + 128 * (mb >> 2)));
+    v.hi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase[1][mb & 3] + 128 * (mb >> 2)));
   }
+  return v;
+}
+
+// O^T[128 dims][16 NB heads] += V^T P^T for one tile, its rescale applied first (P and the
+// factors from LDS).
+template <int NB = 2>
+__device__ __forceinline__ void value_mma(v4f (*acc)[NB], const VFrag& v, const unsigned char* pt,
+                                          const float* alpha) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
   v8bf pf[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -257,12 +265,21 @@ __device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* 
   }
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
-    const v8bf vf = __builtin_bit_cast(v8bf, v8s{lo[mb][0], lo[mb][1], lo[mb][2], lo[mb][3],
-                                                 hi[mb][0], hi[mb][1], hi[mb][2], hi[mb][3]});
+    const v8bf vf = __builtin_bit_cast(v8bf, v8s{v.lo[mb][0], v.lo[mb][1], v.lo[mb][2], v.lo[mb][3],
+                                                 v.hi[mb][0], v.hi[mb][1], v.hi[mb][2], v.hi[mb][3]});
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc[mb][nb], 0, 0, 0);
   }
+}
+
+// Value wave ow, tile j: O^T[128 dims][16 NB heads] += V^T P^T with the rescale of tile j applied
+// first.
+template <int NB = 2>
+__device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* tile, const unsigned char* pt,
+                                           const float* alpha, int ow) {
+  const VFrag v = value_read(tile, ow);
+  value_mma<NB>(acc, v, pt, alpha);
 }
 
 // The selection of token t in ascending position order, slots [kbeg, kbeg + nkeys) of it, into
@@ -988,6 +1005,10 @@ __global__ void __launch_bounds__(512) sfa_kernel64(SfaArgs a) {
   for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  // V^T of tile k is read at the end of step k (the tile landed at that step's barrier) and
+  // multiplied at step k + 1, once P of tile k is published: the reads' latency runs under the
+  // barrier.  Tile k's slot is refilled at step k + 2, after those reads were consumed.
+  VFrag vnext;
   for (int k = 0; k <= nt; ++k) {
     // tile k landed: issued after it are (k >= 1) the index load of step k - 1 and tile k + 1
     if (k < nt) {
@@ -1001,8 +1022,8 @@ __global__ void __launch_bounds__(512) sfa_kernel64(SfaArgs a) {
       issue_tile(k + 2);
       if (k + 3 < nt) tile_offsets(k + 3);             // its indices came with tile k or earlier
     }
-    if (k >= 1)
-      value_tile<4>(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1], ow);
+    if (k >= 1) value_mma<4>(acc, vnext, pbuf[(k - 1) & 1], abuf[(k - 1) & 1]);
+    if (k < nt) vnext = value_read(ring + (k % kNBuf) * kTileB, ow);
   }
   wait_vm<0>();                                        // the index loads past the end
   lds_barrier();                                       // running max and sum published

@@ -199,13 +199,16 @@ def test_sparse_attention_isolated(rng, Hq, T, sink, pad):
         assert not out[1].float().abs().sum().item()
 
 
-@pytest.mark.parametrize("T,k,pad", [(256, 2048, 0.2), (300, 100, 0.0), (257, 32, 0.5), (512, 200, 0.1)])
+@pytest.mark.parametrize("T,k,pad", [(256, 2048, 0.2), (300, 100, 0.0), (257, 32, 0.5), (512, 200, 0.1),
+                                     (256, 64, 0.3), (256, 96, 0.0), (260, 150, 0.2), (256, 190, 0.0),
+                                     (256, 250, 0.1)])
 def test_sparse_attention_64_head_kernel_equals_32_head_kernel(rng, T, k, pad):
     """Batches with one split per token run the 64-head kernel (index ring in LDS, value waves that
-    also gather); it must reproduce the 32-head kernel bit for bit -- the same tiles, per-head
-    arithmetic and order -- on random selections with -1 holes, empty selections, a partial last
-    tile (k = 100), a single tile (k = 32) and fewer tiles than the prologue stages (k < 160),
-    and match the oracle."""
+    also gather and read a tile's V one step early); it must reproduce the 32-head kernel bit for
+    bit -- the same tiles, per-head arithmetic and order -- on random selections with -1 holes,
+    empty selections, every tile count from 1 to 8 (k = 32 .. 250, partial last tiles included:
+    the gather schedule's start and end differ below 3 tiles, the index ring's prologue covers 5)
+    and 64 tiles, and match the oracle."""
     lens = list(rng.integers(300, 5000, size=T))
     sp = Spec(f"sfa64_{T}_{k}", 7400 + T + k, lens, [1] * T, H=8, D=64, k=k, Hq=128)
     wl = make(sp)
