@@ -111,10 +111,10 @@ constexpr int kPP = kKT * 2 + 16;        // P row pitch: 32 keys (a tile) + 16 B
 //    the wave: tile max, P = 2^(z - m) in bf16 and the rescale factor of the accumulators;
 //  * loader waves 2-3: the gather of the tiles into the LDS ring;
 //  * value waves 4-7, wave = value dims 128 (w - 4) .. +127 for all 32 heads: O^T += V^T P^T for
-//    tile k - 1 (V^T through ds_read_b64_tr_b16, P^T from LDS).
+//    tile k - 1 (V^T through ds_read_b64_tr_b16 at the end of step k - 1, P^T from LDS).
 // Step k has one barrier (tile k landed; P and the rescale factors of tile k - 1 published).  P
 // and the factors are double buffered, so the score waves may publish tile k while the value
-// waves still read tile k - 1.  The reference max m only moves when the tile's max exceeds it by
+// waves still read P of tile k - 1.  The reference max m only moves when the tile's max exceeds it by
 // more than kLazy, so P < 2^kLazy and the accumulators are rarely rescaled (the final
 // normalisation uses the same m: exact).
 
@@ -271,15 +271,6 @@ __device__ __forceinline__ void value_mma(v4f (*acc)[NB], const VFrag& v, const 
     for (int nb = 0; nb < NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc[mb][nb], 0, 0, 0);
   }
-}
-
-// Value wave ow, tile j: O^T[128 dims][16 NB heads] += V^T P^T with the rescale of tile j applied
-// first.
-template <int NB = 2>
-__device__ __forceinline__ void value_tile(v4f (*acc)[NB], const unsigned char* tile, const unsigned char* pt,
-                                           const float* alpha, int ow) {
-  const VFrag v = value_read(tile, ow);
-  value_mma<NB>(acc, v, pt, alpha);
 }
 
 // The selection of token t in ascending position order, slots [kbeg, kbeg + nkeys) of it, into
@@ -799,10 +790,13 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
   v4f acc[8][2];                                       // O^T
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) { acc[mb][0] = v4f{0.f, 0.f, 0.f, 0.f}; acc[mb][1] = acc[mb][0]; }
+  // V^T of tile k is read at the end of step k (the tile landed at that step's barrier) and
+  // multiplied at step k + 1 with P of tile k; tile k's slot is refilled at step k + 2
+  VFrag vnext;
   for (int k = 0; k <= nt; ++k) {
     lds_barrier();                                     // P of tile k - 1 published
-    if (k >= 1)
-      value_tile(acc, ring + ((k - 1) % kNBuf) * kTileB, pbuf[(k - 1) & 1], abuf[(k - 1) & 1], wave - 4);
+    if (k >= 1) value_mma<2>(acc, vnext, pbuf[(k - 1) & 1], abuf[(k - 1) & 1]);
+    if (k < nt) vnext = value_read(ring + (k % kNBuf) * kTileB, wave - 4);
   }
   lds_barrier();                                       // running max and sum published
   const int ow = wave - 4;
@@ -865,7 +859,7 @@ __global__ void __launch_bounds__(512) sfa_kernel(SfaArgs a) {
 // and 64 query heads, so each gathered row serves twice the heads of sfa_kernel and the QK^T
 // MFMAs spread over all four SIMDs:
 //  * score waves 0-3, wave = 16 heads (score_tile as in sfa_kernel, one per SIMD);
-//  * value waves 4-7, wave = value dims 128 (w - 4) .. +127 for all 64 heads (value_tile over
+//  * value waves 4-7, wave = value dims 128 (w - 4) .. +127 for all 64 heads (value_mma over
 //    four head blocks), each also gathering 9 of the 36 1-KiB pieces of every tile (no loader
 //    waves: the 8 waves share the SIMDs two by two, so a value wave may take 256 VGPRs).
 // The 8 KiB index stage of sfa_kernel does not fit beside the larger P buffer: the selected
