@@ -293,6 +293,11 @@ dsa_status dsa_indexer_topk(const dsa_batch* batch, int32_t H, int32_t D,
  *   out    device [T, Hq, 512] bf16
  *   ws:    device workspace of at least dsa_sparse_attn_workspace_size(T, Hq, k) bytes,
  *          256-byte aligned (split-K partials); may be NULL when that size is 0.
+ * Schedule (shapes only): the selection is split over workgroups of 32 heads so that a batch
+ * fills the GPU; batches that need no split (one per token) on flat caches with Hq a multiple
+ * of 64 and at least 256 workgroups of 64 heads run a kernel with 64 heads per workgroup
+ * instead, with bit-identical results.  DSA_SFA_H64=0 in the environment keeps the 32-head
+ * kernel (tests).
  */
 size_t dsa_sparse_attn_workspace_size(int32_t num_q, int32_t Hq, int32_t k);
 dsa_status dsa_sparse_attn_decode(const dsa_batch* batch, int32_t Hq, const void* q,
