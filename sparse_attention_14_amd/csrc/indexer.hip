@@ -854,7 +854,10 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hv = lane >> 5, col = lane & 31;
   const int b = blockIdx.y;
-  const int span0 = blockIdx.x * SPAN;
+  // span sx of sequence b, rotated by b: workgroup ids go round-robin to the XCDs, and the
+  // first spans of every sequence (the ones short sequences have) then spread over all of them
+  const int sx = (int)((blockIdx.x + gridDim.x - blockIdx.y % gridDim.x) % gridDim.x);
+  const int span0 = sx * SPAN;
   const int tw0 = (wave / S::BSTR) * NTW;                     // this wave's first token
   const int blk0 = wave % S::BSTR;                             // ... and first block
 
@@ -1213,9 +1216,9 @@ __global__ void __launch_bounds__(kSNW * 64) indexer_stream_kernel(StreamArgs sa
       }
     }
     if constexpr (PRO) {
-      // the prolog's outputs: the group's query codes and scales (workgroup 0 of the sequence),
+      // the prolog's outputs: the group's query codes and scales (span 0 of the sequence),
       // the new key rows of this span
-      if (blockIdx.x == 0) {
+      if (sx == 0) {
         const int qb = nq * H * D;                               // H == HT (compiled shapes)
         for (int o = tid * 16; o < qb; o += NT * 16)
           *reinterpret_cast<uint4*>(sa.pro.q_codes + (long)t0 * H * D + o) = *reinterpret_cast<const uint4*>(qsm + o);
