@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(IdxWaves<G>::value * 64) indexer_kernel(IdxArg
   constexpr int EARLY = SEPQ ? kGroups : 1;
   constexpr unsigned QOFF = SEPQ ? KB : (kGroups - QG) * GB;   // Q's LDS offset
   static_assert(SEPQ || EARLY + QG <= kGroups, "Q staging overlaps the first key group");
-  static_assert(QB <= QG * GB && QB % 1024 == 0 || QB < 1024, "Q staging does not fit");
+  static_assert((QB <= QG * GB && QB % 1024 == 0) || QB < 1024, "Q staging does not fit");
   // Rows past the chunk's last visible key are clamped (never stored).
   const int last_row = maxp - chunk0;
   float wq[NMB][16];                                     // set once the key stream is issued
