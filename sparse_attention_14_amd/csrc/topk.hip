@@ -140,8 +140,16 @@ __global__ void __launch_bounds__(kNT) topk_select(TkArgs a) {
   h[tid] = 0u;
   if (tid < kCW) bw[tid] = 0u;
   if (tid == 0) res[0] = 0xFFFFFFFFu;
-  __syncthreads();
-  find_digit_desc<kNT>(h, (uint32_t)k, sh, res);
+  {
+    // thread tid holds digit kNT + tid, so the digits above it are the threads above it: one
+    // block scan over the registers finds the digit of the k-th largest key in the upper half
+    // (the LDS copy serves the rare lower-half search below)
+    uint32_t all;
+    const uint32_t pre = block_excl_scan<kNT>(x, sh, all);
+    const uint32_t above = all - pre - x;
+    if (above < (uint32_t)k && (uint32_t)k <= above + x) { res[0] = kNT + tid; res[1] = above; }
+    __syncthreads();
+  }
   if (res[0] == 0xFFFFFFFFu) {                            // block-uniform: the lower half too
     uint32_t y = 0;
 #pragma unroll
